@@ -1,0 +1,257 @@
+"""Throughput of the Mixtral sparse-MoE layer forward on one MI355X.
+
+One step = one forward of the layer (router + top-2 + softmax, dispatch
+tables, W1/W3 SwiGLU grouped GEMM, W2 grouped GEMM, combine) over one batch
+of seeded synthetic Mixtral-shape tokens, inputs resident in HBM.  The step is
+issued as the five C-ABI stage calls (the same kernels and launch shapes that
+moe_forward enqueues) so that HIP events on the launch stream can time each
+kernel inside the timed region.
+
+Prints ONE JSON line: the headline workload is 8-token decode (d=4096,
+d_ff=14336, E=8, K=2, bf16); the 512- and 4096-token layers are timed the
+same way and reported under "sweep".  A CPU leg times the float64 oracle on a
+bounded sample (rank 0, N=1 only).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sparse_mixture_experts_32_amd as M  # noqa: E402
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+HEADLINE = "decode_bf16_T8"
+SWEEP = ("mid_bf16_T512", "prefill_bf16_T4096_zipf")
+STAGES = ("router_topk", "route_permute", "expert_swiglu", "expert_down", "combine")
+
+
+class Layer:
+    """Device buffers of one workload and the staged step."""
+
+    def __init__(self, w: W.Workload, dev):
+        self.w = w
+        inp = W.layer_inputs(w, dev)
+        self.x, self.W_g = inp["x"], inp["W_g"]
+        self.W1, self.W3, self.W2 = inp["W1"], inp["W3"], inp["W2"]
+        T, d, d_ff, E, K = w.T, w.d, w.d_ff, w.E, w.K
+        P = T * K
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.topk_idx = torch.empty((T, K), **i32)
+        self.topk_w = torch.empty((T, K), dtype=torch.float32, device=dev)
+        self.offsets = torch.empty(E + 1, **i32)
+        self.sorted_token = torch.empty(P, **i32)
+        self.pos = torch.empty((T, K), **i32)
+        self.H = torch.empty((P, d_ff), dtype=torch.bfloat16, device=dev)
+        self.O = torch.empty((P, d), dtype=torch.float32, device=dev)
+        self.y = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+        self.ws = torch.empty(M.workspace_size(T, d, d_ff, E, K, M.BF16), dtype=torch.uint8,
+                              device=dev)
+
+    def step(self, events=None):
+        w = self.w
+        ev = events or [None] * (len(STAGES) + 1)
+        s = torch.cuda.current_stream()
+
+        def mark(i):
+            if ev[i] is not None:
+                ev[i].record(s)
+
+        mark(0)
+        M.moe_router_topk(self.x, self.W_g, w.K, self.topk_idx, self.topk_w)
+        mark(1)
+        M.moe_route_permute(self.topk_idx, w.E, self.offsets, self.sorted_token, self.pos)
+        mark(2)
+        M.moe_expert_swiglu(self.x, self.W1, self.W3, w.K, self.offsets, self.sorted_token, self.H)
+        mark(3)
+        M.moe_expert_down(self.H, self.W2, w.T, w.K, self.offsets, self.O)
+        mark(4)
+        M.moe_combine(self.O, self.topk_w, self.pos, self.y)
+        mark(5)
+
+    def forward_call(self):
+        w = self.w
+        M.moe_forward(self.x, self.W_g, self.W1, self.W3, self.W2, w.K, y=self.y,
+                      workspace=self.ws)
+
+    def counts(self):
+        off = self.offsets.cpu().numpy()
+        return np.diff(off)
+
+
+def algorithmic(w: W.Workload, counts):
+    """Algorithmic bytes and flops of the layer and of its two GEMM kernels.
+    Bytes count each needed operand once: x, W_g, the weights of experts that
+    received tokens, y; H/O round trips are implementation traffic."""
+    n_act = int(np.sum(np.asarray(counts) > 0))
+    P = w.T * w.K
+    wbytes = w.d * w.d_ff * 2
+    layer_bytes = 2 * w.T * w.d + 2 * w.d * w.E + n_act * 3 * wbytes + 2 * w.T * w.d
+    layer_flops = P * 6 * w.d * w.d_ff + 2 * w.T * w.d * w.E
+    g1_bytes = n_act * 2 * wbytes + 2 * w.T * w.d + P * w.d_ff * 2
+    g1_flops = P * 4 * w.d * w.d_ff
+    g2_bytes = n_act * wbytes + P * w.d_ff * 2 + P * w.d * 4
+    g2_flops = P * 2 * w.d * w.d_ff
+    return dict(n_active=n_act, layer_bytes=layer_bytes, layer_flops=layer_flops,
+                swiglu_bytes=g1_bytes, swiglu_flops=g1_flops, down_bytes=g2_bytes,
+                down_flops=g2_flops)
+
+
+def time_layer(layer: Layer, steps: int, warmup: int):
+    for _ in range(warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        layer.step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_stage = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
+                 for j, name in enumerate(STAGES)}
+    # the single-call path, for reference
+    for _ in range(max(1, warmup // 2)):
+        layer.forward_call()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        layer.forward_call()
+    torch.cuda.synchronize()
+    wall_fwd = time.perf_counter() - t1
+    return wall, per_stage, wall_fwd
+
+
+def roofline_for(w, alg, per_stage_ms):
+    g1_ms = per_stage_ms["expert_swiglu"]
+    intensity = alg["swiglu_flops"] / alg["swiglu_bytes"]
+    if intensity < 312:
+        achieved = alg["swiglu_bytes"] / (g1_ms * 1e-3) / 1e9
+        return dict(kernel="expert_swiglu", bound="hbm", achieved=round(achieved, 1),
+                    peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                    traffic=None, avg_ms=round(g1_ms, 4))
+    achieved = alg["swiglu_flops"] / (g1_ms * 1e-3) / 1e12
+    return dict(kernel="expert_swiglu", bound="mfma", achieved=round(achieved, 1),
+                peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None,
+                avg_ms=round(g1_ms, 4))
+
+
+def cpu_baseline(layer: Layer, max_tokens: int = 8):
+    """Float64 oracle on the first `max_tokens` tokens of the workload (all 8
+    for decode), weights copied to host outside the timed region."""
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    w = layer.w
+    n = min(max_tokens, w.T)
+    x = layer.x[:n].float().cpu().numpy()
+    Wg = layer.W_g.float().cpu().numpy()
+    W1 = [t.float().cpu().numpy() for t in layer.W1]
+    W3 = [t.float().cpu().numpy() for t in layer.W3]
+    W2 = [t.float().cpu().numpy() for t in layer.W2]
+    t0 = time.perf_counter()
+    O.moe_forward(x, Wg, W1, W3, W2, w.K, faithful=True)
+    dt = time.perf_counter() - t0
+    return dict(value=round(n / dt, 3), unit="tokens/s", cores=int(threads), kind="oracle",
+                sample="first %d of %d tokens of %s, float64 oracle, faithful mode, %.2f s"
+                       % (n, w.T, w.name, dt))
+
+
+def run_workload(name, dev, steps, warmup):
+    w = W.WORKLOADS[name]
+    layer = Layer(w, dev)
+    layer.step()
+    torch.cuda.synchronize()
+    counts = layer.counts()
+    wall, per_stage, wall_fwd = time_layer(layer, steps, warmup)
+    alg = algorithmic(w, counts)
+    ms = wall / steps * 1e3
+    res = dict(workload=name, T=w.T, steps=steps, ms_per_step=round(ms, 4),
+               tokens_per_s=round(w.T * steps / wall, 1),
+               ms_per_step_single_call=round(wall_fwd / steps * 1e3, 4),
+               stage_ms={k: round(v, 4) for k, v in per_stage.items()},
+               n_active_experts=alg["n_active"], expert_counts=counts.tolist(),
+               layer_roofline_frac=round(max(alg["layer_bytes"] / (HBM_PEAK_GBS * 1e9),
+                                             alg["layer_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+                                         / (ms * 1e-3), 4),
+               roofline=roofline_for(w, alg, per_stage))
+    return res, layer
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", default=None, help="time just this workload (profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (the MoE layer is not sharded "
+              "across GPUs); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    M.load_library()
+    dev = torch.device("cuda:0")
+
+    if args.only:
+        res, _ = run_workload(args.only, dev, args.steps, args.warmup)
+        print(json.dumps(res), flush=True)
+        return
+
+    head, layer = run_workload(HEADLINE, dev, args.steps, args.warmup)
+    print("# %s done: %.3f ms/step" % (HEADLINE, head["ms_per_step"]), file=sys.stderr,
+          flush=True)
+    cpu = None if args.no_cpu else cpu_baseline(layer)
+    del layer
+    torch.cuda.empty_cache()
+    sweep = []
+    if not args.no_sweep:
+        for name in SWEEP:
+            r, lay = run_workload(name, dev, max(5, args.steps // 5), max(2, args.warmup // 2))
+            print("# %s done: %.3f ms/step" % (name, r["ms_per_step"]), file=sys.stderr,
+                  flush=True)
+            sweep.append(r)
+            del lay
+            torch.cuda.empty_cache()
+    w = W.WORKLOADS[HEADLINE]
+    out = {
+        "metric": "MoE-layer tokens/s at Mixtral shape (T=8/512/4096); % HBM or MFMA peak",
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) unit-RMS tokens, N(0,1/fan_in) weights)",
+        "config": {"workload": HEADLINE, "T": w.T, "d_model": w.d, "d_ff": w.d_ff,
+                   "experts": w.E, "top_k": w.K, "parallelism": "single GPU"},
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
+        "detail": {k: v for k, v in head.items() if k not in ("roofline",)},
+        "sweep": sweep,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

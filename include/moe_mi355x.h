@@ -1,0 +1,178 @@
+/*
+ * moe_mi355x.h -- C ABI of the Mixtral sparse mixture-of-experts layer
+ * forward on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer ("从Mistral 7B到MoE模型Mixtral 8x7B的全面解析：从原理分析到代码解读",
+ * aiqianji.com, section 2.1.1; "Mixtral of Experts", xyznot.com, section
+ * "Method with key equations"):
+ *
+ *     l      = x . W_g                              router logits, no bias
+ *     G(x)   = Softmax(TopK(l))                     TopK masks all but K logits
+ *     y      = sum_i G(x)_i * SwiGLU_i(x)           only experts with G_i > 0
+ *     SwiGLU_i(x) = (SiLU(x W1_i) * (x W3_i)) W2_i  (section 3.2.4, code block D)
+ *
+ * Layout (row-major, the pages' "x . W" orientation):
+ *     x, y      [T, d]
+ *     W_g       [d, E]
+ *     W1[e], W3[e]  [d, d_ff]
+ *     W2[e]     [d_ff, d]
+ * W1, W3, W2 are HOST arrays of E device pointers, read during the call only.
+ * Every other pointer is device memory owned by the caller.  The library
+ * allocates no device memory on these calls; moe_forward carves its
+ * intermediates from the caller's workspace.
+ *
+ * Types: dtype MOE_F32 means float32 storage and float32 arithmetic;
+ * MOE_BF16 means bfloat16 storage with float32 accumulation (bf16 x bf16 ->
+ * fp32 matrix-core products).  Gate weights and logits are float32 in both.
+ *
+ * Errors: arguments are validated on the host before anything is enqueued;
+ * a non-zero status means nothing was launched.  MOE_EHIP reports a launch
+ * failure.  Execution is asynchronous on `stream` (a hipStream_t, NULL = the
+ * default stream): faults surface at the caller's next synchronisation.
+ * Results are bit-identical across runs for identical inputs (no atomics on
+ * any floating-point result).  Inputs must be finite.  Calls on distinct
+ * (stream, workspace) pairs may run concurrently.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+#define MOE_MAX_EXPERTS 64
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,        /* bad pointer, size, K/E, aliasing, alignment */
+  MOE_EUNSUPPORTED = 2,  /* valid but not supported (e.g. bf16 d % 128 != 0) */
+  MOE_EWORKSPACE = 3,    /* workspace missing or smaller than moe_workspace_size */
+  MOE_EHIP = 4           /* a HIP launch reported an error */
+} moe_status;
+
+/* Index of each intermediate inside the workspace; see moe_workspace_layout. */
+typedef enum {
+  MOE_WS_TOPK_IDX = 0,     /* int32 [T, K]   expert of rank r of token t            */
+  MOE_WS_TOPK_W = 1,       /* float [T, K]   gate weight of rank r                  */
+  MOE_WS_OFFSETS = 2,      /* int32 [E + 1]  exclusive scan of pairs per expert     */
+  MOE_WS_SORTED_TOKEN = 3, /* int32 [T*K]    token of each expert-sorted pair       */
+  MOE_WS_POS = 4,          /* int32 [T, K]   sorted position of pair (t, r)         */
+  MOE_WS_H = 5,            /* dtype [T*K, d_ff]  SwiGLU product, expert-sorted rows */
+  MOE_WS_O = 6,            /* float [T*K, d]     expert outputs, expert-sorted rows */
+  MOE_WS_COUNT = 7
+} moe_ws_item;
+
+/* Human-readable name of a status. */
+const char* moe_status_str(moe_status s);
+
+/* Detail of the last error reported on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* MOE_ABI_VERSION of the loaded library. */
+int32_t moe_abi_version(void);
+
+/*
+ * Bytes of workspace moe_forward needs for this shape (256-byte aligned
+ * sub-buffers).  Errors: MOE_EINVAL for bad sizes or a NULL `bytes`.
+ */
+moe_status moe_workspace_size(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K,
+                              int32_t dtype, size_t* bytes);
+
+/*
+ * Byte offset of every intermediate of moe_forward inside the workspace
+ * (offsets[MOE_WS_COUNT]), so a caller can read the routing tables after a
+ * call.  Same shape arguments and errors as moe_workspace_size.
+ */
+moe_status moe_workspace_layout(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K,
+                                int32_t dtype, size_t* offsets);
+
+/*
+ * The whole layer: router + top-K + softmax, dispatch tables, W1/W3 SwiGLU
+ * grouped GEMM, W2 grouped GEMM, gate-weighted combine -- five kernels, no
+ * host synchronisation.
+ *   y_dtype     MOE_F32 or MOE_BF16: storage type of y.  A bf16 layer may
+ *               write fp32 y (the pre-rounding sum); an fp32 layer writes fp32.
+ *   accumulate  0: y = MoE(x).  1: y = round(y + MoE(x)) (residual add).
+ *   workspace   device buffer of at least moe_workspace_size bytes,
+ *               256-byte aligned.
+ * x must not overlap y.  T == 0 returns MOE_OK and launches nothing.
+ * Limits: 1 <= K <= E <= 64; T*K < 2^31; bf16 needs d % 128 == 0,
+ * d_ff % 128 == 0 and 16-byte aligned x, W*, y (else MOE_EUNSUPPORTED).
+ */
+moe_status moe_forward(const void* x, const void* W_g, const void* const* W1,
+                       const void* const* W3, const void* const* W2, int64_t T, int64_t d,
+                       int64_t d_ff, int32_t E, int32_t K, int32_t dtype, void* y,
+                       int32_t y_dtype, int32_t accumulate, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* ---- the five steps, one kernel each, for callers that own the buffers ---- */
+
+/*
+ * Step 1+2 (section 2.1.4: bias-free linear router; section 2.1.1: TopK then
+ * softmax): logits in fp32, the K largest by key (-logit, expert index) so
+ * ties go to the lower index, gate weights = softmax over the K selected.
+ *   topk_idx int32 [T, K], topk_w float [T, K] (rank order), logits float
+ *   [T, E] or NULL.
+ */
+moe_status moe_router_topk(const void* x, const void* W_g, int64_t T, int64_t d, int32_t E,
+                           int32_t K, int32_t dtype, int32_t* topk_idx, float* topk_w,
+                           float* logits, void* stream);
+
+/*
+ * Steps 3-5 (section 3.1.2, code blocks B and C: for each expert the pairs it
+ * processes): stable counting sort of the T*K pairs p = t*K + r by expert.
+ *   offsets int32 [E+1]; sorted_token int32 [T*K] (token ascending inside a
+ *   segment); pos int32 [T, K] = sorted position of pair (t, r).
+ * Bit-exact and deterministic.
+ */
+moe_status moe_route_permute(const int32_t* topk_idx, int64_t T, int32_t E, int32_t K,
+                             int32_t* offsets, int32_t* sorted_token, int32_t* pos,
+                             void* stream);
+
+/*
+ * Step 6 (code block D, first line): for every expert-sorted pair row r of
+ * expert e, H[r] = round(SiLU(x[sorted_token[r]] W1[e]) * (x[...] W3[e])),
+ * fp32 accumulation, one rounding to dtype.  H [T*K, d_ff] in dtype.
+ */
+moe_status moe_expert_swiglu(const void* x, const void* const* W1, const void* const* W3,
+                             int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K,
+                             int32_t dtype, const int32_t* offsets, const int32_t* sorted_token,
+                             void* H, void* stream);
+
+/*
+ * Step 7 (code block D, second line): O[r] = H[r] W2[e] for every sorted row
+ * r of expert e, fp32 accumulation, O float [T*K, d].
+ */
+moe_status moe_expert_down(const void* H, const void* const* W2, int64_t T, int64_t d,
+                           int64_t d_ff, int32_t E, int32_t K, int32_t dtype,
+                           const int32_t* offsets, float* O, void* stream);
+
+/*
+ * Step 8 (section 2.1.1 sum; code block E, zero-initialised accumulator):
+ * s = w[t,0]*O[pos[t,0]], then s = fma(w[t,r], O[pos[t,r]], s) for r = 1..K-1
+ * in fp32; y[t] = round(s), or round(y[t] + s) when accumulate = 1.
+ */
+moe_status moe_combine(const float* O, const float* topk_w, const int32_t* pos, int64_t T,
+                       int64_t d, int32_t K, void* y, int32_t y_dtype, int32_t accumulate,
+                       void* stream);
+
+/*
+ * Pre-norm glue for a stack of blocks ("【DL輪読会】Mixtral of Experts"
+ * slides, "Architecture – 全体": RMSNorm before the MoE block):
+ * out[t] = round(h[t] / sqrt(mean(h[t]^2) + eps)), unit gain, fp32 math.
+ * h and out are [T, d] in dtype and may not overlap.
+ */
+moe_status moe_rmsnorm(const void* h, void* out, int64_t T, int64_t d, float eps, int32_t dtype,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,263 @@
+"""Mixtral sparse-MoE layer forward on AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libmoe_mi355x.so`` (C ABI in
+``include/moe_mi355x.h``).  Every function here only marshals torch tensors
+into pointers, sizes and the current HIP stream; all arithmetic runs in the
+library's HIP kernels.  If the library is missing the functions raise
+``MoeLibraryMissing`` -- there is no fallback path.
+
+The layer ("从Mistral 7B到MoE模型Mixtral 8x7B的全面解析", aiqianji.com, section
+2.1.1): y = sum over the top-K experts of Softmax(TopK(x W_g))_i *
+SwiGLU_i(x), SwiGLU_i(x) = (SiLU(x W1_i) * (x W3_i)) W2_i.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import library_path
+
+__all__ = [
+    "MoeError", "MoeLibraryMissing", "F32", "BF16", "WS_ITEMS",
+    "load_library", "workspace_size", "workspace_layout", "moe_forward",
+    "moe_router_topk", "moe_route_permute", "moe_expert_swiglu", "moe_expert_down",
+    "moe_combine", "moe_rmsnorm", "EXPORTED_SYMBOLS",
+]
+
+F32 = 0
+BF16 = 1
+WS_ITEMS = ("topk_idx", "topk_w", "offsets", "sorted_token", "pos", "H", "O")
+
+EXPORTED_SYMBOLS = (
+    "moe_status_str", "moe_last_error", "moe_abi_version", "moe_workspace_size",
+    "moe_workspace_layout", "moe_forward", "moe_router_topk", "moe_route_permute",
+    "moe_expert_swiglu", "moe_expert_down", "moe_combine", "moe_rmsnorm",
+)
+
+
+class MoeLibraryMissing(RuntimeError):
+    pass
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__("%s: %s" % (name, detail))
+        self.status = status
+        self.name = name
+
+
+_lib = None
+_c_i64 = ctypes.c_int64
+_c_i32 = ctypes.c_int32
+_c_p = ctypes.c_void_p
+_c_sz = ctypes.c_size_t
+
+
+def load_library(path: str | None = None):
+    """Load (once) and return the ctypes handle of libmoe_mi355x.so."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or library_path()
+    if not os.path.exists(path):
+        raise MoeLibraryMissing(
+            "libmoe_mi355x.so not built (expected at %s); run "
+            "`python -m sparse_mixture_experts_32_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    sig = {
+        "moe_status_str": (ctypes.c_char_p, [_c_i32]),
+        "moe_last_error": (ctypes.c_char_p, []),
+        "moe_abi_version": (_c_i32, []),
+        "moe_workspace_size": (_c_i32, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
+                                        ctypes.POINTER(_c_sz)]),
+        "moe_workspace_layout": (_c_i32, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
+                                          ctypes.POINTER(_c_sz)]),
+        "moe_forward": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32,
+                                 _c_i32, _c_i32, _c_p, _c_i32, _c_i32, _c_p, _c_sz, _c_p]),
+        "moe_router_topk": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_p,
+                                     _c_p, _c_p, _c_p]),
+        "moe_route_permute": (_c_i32, [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p]),
+        "moe_expert_swiglu": (_c_i32, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32,
+                                       _c_i32, _c_p, _c_p, _c_p, _c_p]),
+        "moe_expert_down": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
+                                     _c_p, _c_p, _c_p]),
+        "moe_combine": (_c_i32, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_i32, _c_i32,
+                                 _c_p]),
+        "moe_rmsnorm": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, ctypes.c_float, _c_i32, _c_p]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path == library_path():
+        _lib = lib
+    return lib
+
+
+def _check(status: int, lib=None):
+    if status != 0:
+        lib = lib or load_library()
+        raise MoeError(status, lib.moe_status_str(status).decode(),
+                       lib.moe_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError("unsupported dtype %s (bf16 or fp32)" % t.dtype)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _ptr_array(ts):
+    arr = (ctypes.c_void_p * len(ts))(*[_ptr(t) for t in ts])
+    return arr
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def workspace_size(T, d, d_ff, E, K, dtype) -> int:
+    lib = load_library()
+    out = _c_sz(0)
+    _check(lib.moe_workspace_size(T, d, d_ff, E, K, dtype, ctypes.byref(out)), lib)
+    return out.value
+
+
+def workspace_layout(T, d, d_ff, E, K, dtype) -> dict:
+    lib = load_library()
+    arr = (_c_sz * len(WS_ITEMS))()
+    _check(lib.moe_workspace_layout(T, d, d_ff, E, K, dtype, arr), lib)
+    return dict(zip(WS_ITEMS, list(arr)))
+
+
+def workspace_views(ws: torch.Tensor, T, d, d_ff, E, K, dtype) -> dict:
+    """Typed views of the intermediates moe_forward leaves in a workspace."""
+    off = workspace_layout(T, d, d_ff, E, K, dtype)
+    P = T * K
+    hdt = torch.bfloat16 if dtype == BF16 else torch.float32
+
+    def view(name, n, dt):
+        nbytes = n * torch.empty((), dtype=dt).element_size()
+        return ws[off[name]:off[name] + nbytes].view(dt)
+
+    return dict(
+        topk_idx=view("topk_idx", P, torch.int32).view(T, K),
+        topk_w=view("topk_w", P, torch.float32).view(T, K),
+        offsets=view("offsets", E + 1, torch.int32),
+        sorted_token=view("sorted_token", P, torch.int32),
+        pos=view("pos", P, torch.int32).view(T, K),
+        H=view("H", P * d_ff, hdt).view(P, d_ff),
+        O=view("O", P * d, torch.float32).view(P, d),
+    )
+
+
+def moe_forward(x, W_g, W1, W3, W2, K, y=None, y_dtype=None, accumulate=False, workspace=None,
+                stream=None):
+    """y = MoE(x) (or y += MoE(x) with accumulate=True) through the HIP kernels.
+
+    x [T, d], W_g [d, E], W1[e]/W3[e] [d, d_ff], W2[e] [d_ff, d]: bf16 or fp32
+    CUDA tensors of one dtype.  y_dtype defaults to x's dtype; a bf16 layer
+    may write fp32 y.  Returns y."""
+    lib = load_library()
+    T, d = x.shape
+    E = len(W1)
+    d_ff = W1[0].shape[1]
+    dt = _dtype_code(x)
+    if y is None:
+        ydt = x.dtype if y_dtype is None else y_dtype
+        y = torch.empty((T, d), dtype=ydt, device=x.device)
+    ycode = _dtype_code(y)
+    need = workspace_size(T, d, d_ff, E, K, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(lib.moe_forward(_ptr(x), _ptr(W_g), _ptr_array(W1), _ptr_array(W3), _ptr_array(W2),
+                           T, d, d_ff, E, K, dt, _ptr(y), ycode, 1 if accumulate else 0,
+                           _ptr(workspace), workspace.numel(), _stream(stream)), lib)
+    return y
+
+
+def moe_router_topk(x, W_g, K, topk_idx=None, topk_w=None, logits=None, stream=None):
+    lib = load_library()
+    T, d = x.shape
+    E = W_g.shape[1]
+    if topk_idx is None:
+        topk_idx = torch.empty((T, K), dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, K), dtype=torch.float32, device=x.device)
+    _check(lib.moe_router_topk(_ptr(x), _ptr(W_g), T, d, E, K, _dtype_code(x), _ptr(topk_idx),
+                               _ptr(topk_w), _ptr(logits), _stream(stream)), lib)
+    return topk_idx, topk_w
+
+
+def moe_route_permute(topk_idx, E, offsets=None, sorted_token=None, pos=None, stream=None):
+    lib = load_library()
+    T, K = topk_idx.shape
+    dev = topk_idx.device
+    if offsets is None:
+        offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    if sorted_token is None:
+        sorted_token = torch.empty(T * K, dtype=torch.int32, device=dev)
+    if pos is None:
+        pos = torch.empty((T, K), dtype=torch.int32, device=dev)
+    _check(lib.moe_route_permute(_ptr(topk_idx), T, E, K, _ptr(offsets), _ptr(sorted_token),
+                                 _ptr(pos), _stream(stream)), lib)
+    return offsets, sorted_token, pos
+
+
+def moe_expert_swiglu(x, W1, W3, K, offsets, sorted_token, H=None, stream=None):
+    lib = load_library()
+    T, d = x.shape
+    E = len(W1)
+    d_ff = W1[0].shape[1]
+    if H is None:
+        H = torch.empty((T * K, d_ff), dtype=x.dtype, device=x.device)
+    _check(lib.moe_expert_swiglu(_ptr(x), _ptr_array(W1), _ptr_array(W3), T, d, d_ff, E, K,
+                                 _dtype_code(x), _ptr(offsets), _ptr(sorted_token), _ptr(H),
+                                 _stream(stream)), lib)
+    return H
+
+
+def moe_expert_down(H, W2, T, K, offsets, O=None, stream=None):
+    lib = load_library()
+    E = len(W2)
+    d_ff, d = W2[0].shape
+    if O is None:
+        O = torch.empty((T * K, d), dtype=torch.float32, device=H.device)
+    _check(lib.moe_expert_down(_ptr(H), _ptr_array(W2), T, d, d_ff, E, K, _dtype_code(H),
+                               _ptr(offsets), _ptr(O), _stream(stream)), lib)
+    return O
+
+
+def moe_combine(O, topk_w, pos, y=None, y_dtype=torch.float32, accumulate=False, stream=None):
+    lib = load_library()
+    T, K = topk_w.shape
+    d = O.shape[1]
+    if y is None:
+        y = torch.empty((T, d), dtype=y_dtype, device=O.device)
+    _check(lib.moe_combine(_ptr(O), _ptr(topk_w), _ptr(pos), T, d, K, _ptr(y), _dtype_code(y),
+                           1 if accumulate else 0, _stream(stream)), lib)
+    return y
+
+
+def moe_rmsnorm(h, out=None, eps=1e-5, stream=None):
+    lib = load_library()
+    T, d = h.shape
+    if out is None:
+        out = torch.empty_like(h)
+    _check(lib.moe_rmsnorm(_ptr(h), _ptr(out), T, d, eps, _dtype_code(h), _stream(stream)), lib)
+    return out

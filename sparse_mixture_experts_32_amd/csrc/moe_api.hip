@@ -1,0 +1,323 @@
+// C ABI of the MoE layer forward: host-side validation, workspace carving and
+// the launch sequence.  Declarations and contracts: include/moe_mi355x.h.
+#include <algorithm>
+#include <cstdarg>
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <unordered_set>
+
+#include "../../include/moe_mi355x.h"
+#include "moe_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+moe_status fail(moe_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+moe_status ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Status of a finished launch sequence: MOE_OK (and a cleared message) or MOE_EHIP.
+moe_status finish(hipError_t e, const char* what) {
+  return e == hipSuccess ? ok() : hip_status(e, what);
+}
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t dtype_bytes(int32_t dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+moe_status check_dtype(int32_t dt, const char* name) {
+  if (dt != MOE_F32 && dt != MOE_BF16) return fail(MOE_EINVAL, "unknown %s %d", name, dt);
+  return MOE_OK;
+}
+
+moe_status check_shape(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K, int32_t dt) {
+  moe_status s = check_dtype(dt, "dtype");
+  if (s) return s;
+  if (T < 0) return fail(MOE_EINVAL, "T = %lld < 0", (long long)T);
+  if (d <= 0 || d_ff <= 0) return fail(MOE_EINVAL, "d and d_ff must be positive");
+  if (E < 1 || E > MOE_MAX_EXPERTS)
+    return fail(MOE_EINVAL, "E = %d outside [1, %d]", E, MOE_MAX_EXPERTS);
+  if (K < 1 || K > E) return fail(MOE_EINVAL, "K = %d outside [1, E = %d]", K, E);
+  if (T * (int64_t)K >= (int64_t(1) << 31)) return fail(MOE_EINVAL, "T*K must be < 2^31");
+  if (d >= (int64_t(1) << 31) || d_ff >= (int64_t(1) << 31))
+    return fail(MOE_EINVAL, "d and d_ff must be < 2^31");
+  if (dt == MOE_BF16 && (d % 128 != 0 || d_ff % 128 != 0))
+    return fail(MOE_EUNSUPPORTED, "bf16 path needs d %% 128 == 0 and d_ff %% 128 == 0");
+  return MOE_OK;
+}
+
+void layout(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K, int32_t dt,
+            size_t off[MOE_WS_COUNT], size_t* total) {
+  const size_t P = (size_t)T * K;
+  size_t o = 0;
+  auto put = [&](int item, size_t bytes) {
+    off[item] = o;
+    o = align256(o + bytes);
+  };
+  put(MOE_WS_TOPK_IDX, P * 4);
+  put(MOE_WS_TOPK_W, P * 4);
+  put(MOE_WS_OFFSETS, (size_t)(E + 1) * 4);
+  put(MOE_WS_SORTED_TOKEN, P * 4);
+  put(MOE_WS_POS, P * 4);
+  put(MOE_WS_H, P * (size_t)d_ff * dtype_bytes(dt));
+  put(MOE_WS_O, P * (size_t)d * 4);
+  *total = o;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+moe_status fill_ptrs(const void* const* src, int32_t E, moe::ExpertPtrs& dst, const char* name,
+                     bool need16) {
+  if (!src) return fail(MOE_EINVAL, "%s is NULL", name);
+  std::memset(&dst, 0, sizeof(dst));
+  for (int e = 0; e < E; ++e) {
+    if (!src[e]) return fail(MOE_EINVAL, "%s[%d] is NULL", name, e);
+    if (need16 && !aligned16(src[e]))
+      return fail(MOE_EUNSUPPORTED, "%s[%d] is not 16-byte aligned", name, e);
+    dst.p[e] = src[e];
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+namespace moe {
+
+hipError_t allow_dynamic_lds(const void* kernel, int bytes) {
+  static std::mutex mu;
+  static std::unordered_set<uint64_t> done;
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const uint64_t key = (reinterpret_cast<uint64_t>(kernel) << 8) ^ (uint64_t)dev;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count(key)) return hipSuccess;
+  err = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (err == hipSuccess) done.insert(key);
+  return err;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE";
+    case MOE_EHIP: return "MOE_EHIP";
+  }
+  return "MOE_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+moe_status moe_workspace_size(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K,
+                              int32_t dtype, size_t* bytes) {
+  if (!bytes) return fail(MOE_EINVAL, "bytes is NULL");
+  moe_status s = check_shape(T, d, d_ff, E, K, dtype);
+  if (s) return s;
+  size_t off[MOE_WS_COUNT];
+  layout(T, d, d_ff, E, K, dtype, off, bytes);
+  return ok();
+}
+
+moe_status moe_workspace_layout(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K,
+                                int32_t dtype, size_t* offsets) {
+  if (!offsets) return fail(MOE_EINVAL, "offsets is NULL");
+  moe_status s = check_shape(T, d, d_ff, E, K, dtype);
+  if (s) return s;
+  size_t total;
+  layout(T, d, d_ff, E, K, dtype, offsets, &total);
+  return ok();
+}
+
+moe_status moe_router_topk(const void* x, const void* W_g, int64_t T, int64_t d, int32_t E,
+                           int32_t K, int32_t dtype, int32_t* topk_idx, float* topk_w,
+                           float* logits, void* stream) {
+  moe_status s = check_dtype(dtype, "dtype");
+  if (s) return s;
+  if (T < 0 || d <= 0 || d >= (int64_t(1) << 31)) return fail(MOE_EINVAL, "bad T or d");
+  if (E < 1 || E > MOE_MAX_EXPERTS || K < 1 || K > E) return fail(MOE_EINVAL, "bad E or K");
+  if (T * (int64_t)K >= (int64_t(1) << 31)) return fail(MOE_EINVAL, "T*K must be < 2^31");
+  if (T == 0) return ok();
+  if (!x || !W_g || !topk_idx || !topk_w) return fail(MOE_EINVAL, "NULL pointer");
+  return finish(moe::launch_router_topk(x, W_g, (int)T, (int)d, E, K, dtype, topk_idx,
+                                            topk_w, logits, (hipStream_t)stream),
+                    "router_topk");
+}
+
+moe_status moe_route_permute(const int32_t* topk_idx, int64_t T, int32_t E, int32_t K,
+                             int32_t* offsets, int32_t* sorted_token, int32_t* pos,
+                             void* stream) {
+  if (T < 0) return fail(MOE_EINVAL, "T < 0");
+  if (E < 1 || E > MOE_MAX_EXPERTS || K < 1 || K > E) return fail(MOE_EINVAL, "bad E or K");
+  if (T * (int64_t)K >= (int64_t(1) << 31)) return fail(MOE_EINVAL, "T*K must be < 2^31");
+  if (!offsets) return fail(MOE_EINVAL, "offsets is NULL");
+  if (T > 0 && (!topk_idx || !sorted_token || !pos)) return fail(MOE_EINVAL, "NULL pointer");
+  return finish(moe::launch_route_permute(topk_idx, (int)T, E, K, offsets, sorted_token, pos,
+                                              (hipStream_t)stream),
+                    "route_permute");
+}
+
+moe_status moe_expert_swiglu(const void* x, const void* const* W1, const void* const* W3,
+                             int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K,
+                             int32_t dtype, const int32_t* offsets, const int32_t* sorted_token,
+                             void* H, void* stream) {
+  moe_status s = check_shape(T, d, d_ff, E, K, dtype);
+  if (s) return s;
+  if (T == 0) return ok();
+  if (!x || !offsets || !sorted_token || !H) return fail(MOE_EINVAL, "NULL pointer");
+  const bool bf16 = dtype == MOE_BF16;
+  if (bf16 && (!aligned16(x) || !aligned16(H)))
+    return fail(MOE_EUNSUPPORTED, "x and H must be 16-byte aligned");
+  moe::ExpertPtrs p1, p3;
+  if ((s = fill_ptrs(W1, E, p1, "W1", bf16))) return s;
+  if ((s = fill_ptrs(W3, E, p3, "W3", bf16))) return s;
+  const int P = (int)(T * K);
+  hipError_t e = bf16 ? moe::launch_expert_swiglu_bf16(x, sorted_token, p1, p3, offsets, P, (int)d,
+                                                       (int)d_ff, E, H, (hipStream_t)stream)
+                      : moe::launch_expert_swiglu_f32(x, sorted_token, p1, p3, offsets, P, (int)d,
+                                                      (int)d_ff, E, H, (hipStream_t)stream);
+  return finish(e, "expert_swiglu");
+}
+
+moe_status moe_expert_down(const void* H, const void* const* W2, int64_t T, int64_t d,
+                           int64_t d_ff, int32_t E, int32_t K, int32_t dtype,
+                           const int32_t* offsets, float* O, void* stream) {
+  moe_status s = check_shape(T, d, d_ff, E, K, dtype);
+  if (s) return s;
+  if (T == 0) return ok();
+  if (!H || !offsets || !O) return fail(MOE_EINVAL, "NULL pointer");
+  const bool bf16 = dtype == MOE_BF16;
+  if (bf16 && (!aligned16(H) || !aligned16(O)))
+    return fail(MOE_EUNSUPPORTED, "H and O must be 16-byte aligned");
+  moe::ExpertPtrs p2;
+  if ((s = fill_ptrs(W2, E, p2, "W2", bf16))) return s;
+  const int P = (int)(T * K);
+  hipError_t e = bf16 ? moe::launch_expert_down_bf16(H, p2, offsets, P, (int)d, (int)d_ff, E, O,
+                                                     (hipStream_t)stream)
+                      : moe::launch_expert_down_f32(H, p2, offsets, P, (int)d, (int)d_ff, E, O,
+                                                    (hipStream_t)stream);
+  return finish(e, "expert_down");
+}
+
+moe_status moe_combine(const float* O, const float* topk_w, const int32_t* pos, int64_t T,
+                       int64_t d, int32_t K, void* y, int32_t y_dtype, int32_t accumulate,
+                       void* stream) {
+  moe_status s = check_dtype(y_dtype, "y_dtype");
+  if (s) return s;
+  if (T < 0 || d <= 0 || d >= (int64_t(1) << 31) || K < 1 || K > MOE_MAX_EXPERTS)
+    return fail(MOE_EINVAL, "bad T, d or K");
+  if (T == 0) return ok();
+  if (!O || !topk_w || !pos || !y) return fail(MOE_EINVAL, "NULL pointer");
+  if (d % 4 == 0 && (!aligned16(O) || (y_dtype == MOE_F32 ? !aligned16(y) : ((uintptr_t)y & 7))))
+    return fail(MOE_EUNSUPPORTED, "O must be 16-byte and y vector aligned");
+  return finish(moe::launch_combine(O, topk_w, pos, (int)T, (int)d, K, y, y_dtype,
+                                        accumulate ? 1 : 0, (hipStream_t)stream),
+                    "combine");
+}
+
+moe_status moe_rmsnorm(const void* h, void* out, int64_t T, int64_t d, float eps, int32_t dtype,
+                       void* stream) {
+  moe_status s = check_dtype(dtype, "dtype");
+  if (s) return s;
+  if (T < 0 || d <= 0 || d >= (int64_t(1) << 31)) return fail(MOE_EINVAL, "bad T or d");
+  if (!(eps >= 0.0f)) return fail(MOE_EINVAL, "eps must be >= 0");
+  if (T == 0) return ok();
+  if (!h || !out) return fail(MOE_EINVAL, "NULL pointer");
+  const size_t bytes = (size_t)T * d * dtype_bytes(dtype);
+  if (overlap(h, bytes, out, bytes)) return fail(MOE_EINVAL, "h and out overlap");
+  return finish(moe::launch_rmsnorm(h, out, (int)T, (int)d, eps, dtype, (hipStream_t)stream),
+                    "rmsnorm");
+}
+
+moe_status moe_forward(const void* x, const void* W_g, const void* const* W1,
+                       const void* const* W3, const void* const* W2, int64_t T, int64_t d,
+                       int64_t d_ff, int32_t E, int32_t K, int32_t dtype, void* y,
+                       int32_t y_dtype, int32_t accumulate, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  moe_status s = check_shape(T, d, d_ff, E, K, dtype);
+  if (s) return s;
+  if ((s = check_dtype(y_dtype, "y_dtype"))) return s;
+  if (dtype == MOE_F32 && y_dtype != MOE_F32)
+    return fail(MOE_EUNSUPPORTED, "an fp32 layer writes fp32 y");
+  if (T == 0) return ok();
+  if (!x || !W_g || !y) return fail(MOE_EINVAL, "NULL pointer");
+  const bool bf16 = dtype == MOE_BF16;
+  moe::ExpertPtrs p1, p3, p2;
+  if ((s = fill_ptrs(W1, E, p1, "W1", bf16))) return s;
+  if ((s = fill_ptrs(W3, E, p3, "W3", bf16))) return s;
+  if ((s = fill_ptrs(W2, E, p2, "W2", bf16))) return s;
+  if (bf16 && (!aligned16(x) || !aligned16(y)))
+    return fail(MOE_EUNSUPPORTED, "x and y must be 16-byte aligned");
+  const size_t xbytes = (size_t)T * d * dtype_bytes(dtype);
+  const size_t ybytes = (size_t)T * d * dtype_bytes(y_dtype);
+  if (overlap(x, xbytes, y, ybytes)) return fail(MOE_EINVAL, "x and y overlap");
+  size_t off[MOE_WS_COUNT], need;
+  layout(T, d, d_ff, E, K, dtype, off, &need);
+  if (!workspace) return fail(MOE_EWORKSPACE, "workspace is NULL");
+  if (workspace_bytes < need)
+    return fail(MOE_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MOE_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (overlap(workspace, need, x, xbytes) || overlap(workspace, need, y, ybytes))
+    return fail(MOE_EINVAL, "workspace overlaps x or y");
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* topk_idx = reinterpret_cast<int32_t*>(ws + off[MOE_WS_TOPK_IDX]);
+  float* topk_w = reinterpret_cast<float*>(ws + off[MOE_WS_TOPK_W]);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + off[MOE_WS_OFFSETS]);
+  int32_t* sorted_token = reinterpret_cast<int32_t*>(ws + off[MOE_WS_SORTED_TOKEN]);
+  int32_t* pos = reinterpret_cast<int32_t*>(ws + off[MOE_WS_POS]);
+  void* H = ws + off[MOE_WS_H];
+  float* O = reinterpret_cast<float*>(ws + off[MOE_WS_O]);
+  hipStream_t st = (hipStream_t)stream;
+  const int P = (int)(T * K);
+
+  hipError_t e = moe::launch_router_topk(x, W_g, (int)T, (int)d, E, K, dtype, topk_idx, topk_w,
+                                         nullptr, st);
+  if (e != hipSuccess) return hip_status(e, "router_topk");
+  e = moe::launch_route_permute(topk_idx, (int)T, E, K, offsets, sorted_token, pos, st);
+  if (e != hipSuccess) return hip_status(e, "route_permute");
+  e = bf16 ? moe::launch_expert_swiglu_bf16(x, sorted_token, p1, p3, offsets, P, (int)d,
+                                            (int)d_ff, E, H, st)
+           : moe::launch_expert_swiglu_f32(x, sorted_token, p1, p3, offsets, P, (int)d, (int)d_ff,
+                                           E, H, st);
+  if (e != hipSuccess) return hip_status(e, "expert_swiglu");
+  e = bf16 ? moe::launch_expert_down_bf16(H, p2, offsets, P, (int)d, (int)d_ff, E, O, st)
+           : moe::launch_expert_down_f32(H, p2, offsets, P, (int)d, (int)d_ff, E, O, st);
+  if (e != hipSuccess) return hip_status(e, "expert_down");
+  e = moe::launch_combine(O, topk_w, pos, (int)T, (int)d, K, y, y_dtype, accumulate ? 1 : 0, st);
+  if (e != hipSuccess) return hip_status(e, "combine");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// Launchers of the MoE kernels; the C ABI in moe_api.hip validates arguments
+// and calls these.  All sizes here have been checked by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_common.h"
+
+namespace moe {
+
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+hipError_t launch_router_topk(const void* x, const void* Wg, int T, int d, int E, int K,
+                              int dtype, int32_t* topk_idx, float* topk_w, float* logits,
+                              hipStream_t stream);
+
+hipError_t launch_route_permute(const int32_t* topk_idx, int T, int E, int K, int32_t* offsets,
+                                int32_t* sorted_token, int32_t* pos, hipStream_t stream);
+
+// a6: H[r] = round(SiLU(A[r] W1[e]) * (A[r] W3[e])) over the expert-sorted
+// rows r of expert e, A[r] = x[sorted_token[r]].
+hipError_t launch_expert_swiglu_bf16(const void* x, const int32_t* sorted_token,
+                                     const ExpertPtrs& W1, const ExpertPtrs& W3,
+                                     const int32_t* offsets, int P, int d, int d_ff, int E,
+                                     void* H, hipStream_t stream);
+hipError_t launch_expert_swiglu_f32(const void* x, const int32_t* sorted_token,
+                                    const ExpertPtrs& W1, const ExpertPtrs& W3,
+                                    const int32_t* offsets, int P, int d, int d_ff, int E,
+                                    void* H, hipStream_t stream);
+
+// a7: O[r] = H[r] W2[e] over expert-sorted rows, fp32 O.
+hipError_t launch_expert_down_bf16(const void* H, const ExpertPtrs& W2, const int32_t* offsets,
+                                   int P, int d, int d_ff, int E, float* O, hipStream_t stream);
+hipError_t launch_expert_down_f32(const void* H, const ExpertPtrs& W2, const int32_t* offsets,
+                                  int P, int d, int d_ff, int E, float* O, hipStream_t stream);
+
+// Lets `kernel` use `bytes` of dynamic LDS on the current device (once per
+// device and kernel).
+hipError_t allow_dynamic_lds(const void* kernel, int bytes);
+
+hipError_t launch_combine(const float* O, const float* topk_w, const int32_t* pos, int T, int d,
+                          int K, void* y, int y_dtype, int accumulate, hipStream_t stream);
+
+hipError_t launch_rmsnorm(const void* h, void* out, int T, int d, float eps, int dtype,
+                          hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,132 @@
+"""Host-side checks of the C-ABI library: it loads, exports every entry point
+the header declares, and rejects bad arguments before launching anything.
+
+Only argument combinations that fail validation are passed here (with fake,
+never-dereferenced addresses), so no kernel is ever launched by these tests.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_mixture_experts_32_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE = 0, 1, 2, 3
+FAKE = 0x7F0000000000          # 256-byte aligned fake device address (never used)
+FAKE2 = 0x7F0100000000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(M.build.library_path()):
+        pytest.fail("libmoe_mi355x.so is not built; run python -m sparse_mixture_experts_32_amd.build")
+    return M.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(M.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", M.build.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.moe_abi_version() == 1
+    assert lib.moe_status_str(0) == b"MOE_OK"
+    assert lib.moe_status_str(4) == b"MOE_EHIP"
+
+
+def test_workspace_size_and_layout(lib):
+    n = ctypes.c_size_t()
+    assert lib.moe_workspace_size(4096, 4096, 14336, 8, 2, 1, ctypes.byref(n)) == OK
+    lay = M.workspace_layout(4096, 4096, 14336, 8, 2, 1)
+    P = 8192
+    assert lay["topk_idx"] == 0 and all(v % 256 == 0 for v in lay.values())
+    assert lay["O"] - lay["H"] >= P * 14336 * 2
+    assert n.value >= lay["O"] + P * 4096 * 4
+    assert lib.moe_workspace_size(8, 4096, 14336, 8, 2, 1, None) == EINVAL
+    assert lib.moe_workspace_size(8, 4000, 14336, 8, 2, 1, ctypes.byref(n)) == EUNSUPPORTED
+    assert lib.moe_workspace_size(8, 4000, 14300, 8, 2, 0, ctypes.byref(n)) == OK  # fp32: any d
+
+
+def _forward(lib, T=8, d=256, d_ff=256, E=8, K=2, dt=1, x=FAKE, y=FAKE2, ydt=None, ws=0x7F0200000000,
+             ws_bytes=1 << 40, w_ptrs=None, wg=FAKE):
+    ptrs = w_ptrs if w_ptrs is not None else [FAKE + 4096 * (i + 1) for i in range(E)]
+    arr = (ctypes.c_void_p * len(ptrs))(*ptrs)
+    return lib.moe_forward(x, wg, arr, arr, arr, T, d, d_ff, E, K, dt, y,
+                           dt if ydt is None else ydt, 0, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(x=None), EINVAL),
+    (dict(wg=None), EINVAL),
+    (dict(y=None), EINVAL),
+    (dict(K=0), EINVAL),
+    (dict(K=9), EINVAL),
+    (dict(E=65, K=2), EINVAL),
+    (dict(T=-1), EINVAL),
+    (dict(dt=7), EINVAL),
+    (dict(ydt=5), EINVAL),
+    (dict(d=200), EUNSUPPORTED),
+    (dict(d_ff=300), EUNSUPPORTED),
+    (dict(dt=0, ydt=1), EUNSUPPORTED),
+    (dict(x=FAKE + 2), EUNSUPPORTED),
+    (dict(y=FAKE), EINVAL),                       # x aliases y
+    (dict(ws=None), EWORKSPACE),
+    (dict(ws_bytes=100), EWORKSPACE),
+    (dict(ws=0x7F0200000010), EWORKSPACE),        # not 256-byte aligned
+    (dict(ws=FAKE), EINVAL),                      # workspace overlaps x
+    (dict(w_ptrs=[FAKE] * 7 + [0]), EINVAL),       # a NULL expert pointer
+    (dict(w_ptrs=[FAKE + 2] * 8), EUNSUPPORTED),   # misaligned expert pointer
+])
+def test_forward_rejects_before_launch(lib, kwargs, status):
+    got = _forward(lib, **kwargs)
+    assert got == status, lib.moe_last_error()
+    assert lib.moe_last_error() != b""
+
+
+def test_forward_empty_batch_is_a_noop(lib):
+    assert _forward(lib, T=0) == OK
+    assert lib.moe_last_error() == b""
+
+
+def test_stage_entry_points_validate(lib):
+    arr = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    assert lib.moe_router_topk(FAKE, FAKE, 4, 64, 8, 0, 1, FAKE, FAKE, None, None) == EINVAL
+    assert lib.moe_router_topk(FAKE, FAKE, 4, 64, 8, 2, 3, FAKE, FAKE, None, None) == EINVAL
+    assert lib.moe_router_topk(None, FAKE, 4, 64, 8, 2, 1, FAKE, FAKE, None, None) == EINVAL
+    assert lib.moe_route_permute(FAKE, 4, 65, 2, FAKE, FAKE, FAKE, None) == EINVAL
+    assert lib.moe_route_permute(FAKE, 4, 8, 2, None, FAKE, FAKE, None) == EINVAL
+    assert lib.moe_expert_swiglu(FAKE, arr, arr, 4, 100, 256, 8, 2, 1, FAKE, FAKE, FAKE,
+                                 None) == EUNSUPPORTED
+    assert lib.moe_expert_swiglu(FAKE, arr, arr, 4, 128, 256, 8, 2, 1, None, FAKE, FAKE,
+                                 None) == EINVAL
+    assert lib.moe_expert_down(FAKE, arr, 4, 128, 256, 8, 2, 1, FAKE, None, None) == EINVAL
+    assert lib.moe_combine(FAKE, FAKE, FAKE, 4, 128, 0, FAKE2, 0, 0, None) == EINVAL
+    assert lib.moe_combine(FAKE, FAKE, FAKE, 4, 128, 2, None, 0, 0, None) == EINVAL
+    assert lib.moe_rmsnorm(FAKE, FAKE, 4, 128, 1e-5, 1, None) == EINVAL     # overlap
+    assert lib.moe_rmsnorm(FAKE, FAKE2, 4, 128, -1.0, 1, None) == EINVAL
+    for fn_args in [(FAKE, FAKE, 0, 64, 8, 2, 1, FAKE, FAKE, None, None)]:
+        assert lib.moe_router_topk(*fn_args) == OK      # T = 0: nothing launched
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(M.MoeLibraryMissing):
+        M.load_library(str(tmp_path / "missing.so"))

@@ -1,0 +1,314 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+Inputs come from the seeded generators in ``workloads``; the oracle gets the
+same bytes (upcast exactly to float) and never sees a HIP output.  Rules and
+tolerances: ``tests/parity.py``.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_mixture_experts_32_amd as M
+import workloads as W
+from oracle import moe_oracle as O
+from tests import parity as PY
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+class LazyNp:
+    """Converts expert matrices to float numpy only when the oracle asks."""
+
+    def __init__(self, ts):
+        self.ts = ts
+
+    def __len__(self):
+        return len(self.ts)
+
+    def __getitem__(self, e):
+        return PY.to_np(self.ts[e])
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    M.load_library()
+    return torch.device("cuda:0")
+
+
+def small(name="mid_bf16_T512", **kw):
+    return W.scaled(W.WORKLOADS[name], **kw)
+
+
+def run_forward(inp, K, y_dtype=torch.float32, y=None, accumulate=False):
+    x = inp["x"]
+    T, d = x.shape
+    E = len(inp["W1"])
+    d_ff = inp["W1"][0].shape[1]
+    dt = M.BF16 if x.dtype == torch.bfloat16 else M.F32
+    ws = torch.empty(max(M.workspace_size(T, d, d_ff, E, K, dt), 1), dtype=torch.uint8,
+                     device=x.device)
+    y = M.moe_forward(x, inp["W_g"], inp["W1"], inp["W3"], inp["W2"], K, y=y, y_dtype=y_dtype,
+                      accumulate=accumulate, workspace=ws)
+    torch.cuda.synchronize()
+    views = M.workspace_views(ws, T, d, d_ff, E, K, dt) if T > 0 else {}
+    return y, {k: v.clone() for k, v in views.items()}
+
+
+def oracle(inp, K, faithful, tokens=None):
+    x = PY.to_np(inp["x"])
+    if tokens is not None:
+        x = x[tokens]
+    return O.moe_forward(x, PY.to_np(inp["W_g"]), LazyNp(inp["W1"]), LazyNp(inp["W3"]),
+                         LazyNp(inp["W2"]), K, faithful=faithful)
+
+
+def check_layer(inp, K, tokens=None, bf16_store=True):
+    x = inp["x"]
+    is_bf16 = x.dtype == torch.bfloat16
+    T = x.shape[0]
+    E = len(inp["W1"])
+    y32, v = run_forward(inp, K, torch.float32)
+    rows = np.arange(T) if tokens is None else np.asarray(tokens)
+    y_ref, aux = oracle(inp, K, faithful=is_bf16, tokens=rows)
+    set_ok = PY.check_routing(v["topk_idx"].cpu().numpy()[rows], v["topk_w"].cpu().numpy()[rows],
+                              aux["idx"], aux["w"], aux["logits"], K)
+    err = PY.rel_err(PY.to_np(y32)[rows], y_ref, set_ok)
+    tol = PY.TOL_BF16 if is_bf16 else PY.TOL_F32
+    say("rel err %.3e (tol %.0e) over %d decided of %d tokens" % (err, tol, set_ok.sum(), len(rows)))
+    assert err <= tol
+    if tokens is None:
+        keep = np.zeros(T, dtype=bool)
+        keep[rows[set_ok]] = True
+        PY.check_permutation(v["offsets"].cpu().numpy(), v["sorted_token"].cpu().numpy(),
+                             aux["idx"], E, K, keep)
+    if is_bf16 and bf16_store:
+        yb, _ = run_forward(inp, K, torch.bfloat16)
+        assert torch.equal(yb, PY.bf16_rne_of(y32))
+    return y32, v, err
+
+
+# ---------------------------------------------------------------- router
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_router_small(dev, dtype):
+    w = small(T=300, d=256, d_ff=128, dtype=dtype)
+    say("router", dtype, w.T, w.d)
+    W_g, _, _, _ = W.expert_weights(w, dev, experts=[])
+    x = W.make_x(w, W_g, dev)
+    logits = torch.empty((w.T, w.E), dtype=torch.float32, device=dev)
+    idx, wt = M.moe_router_topk(x, W_g, 2, logits=logits)
+    torch.cuda.synchronize()
+    l64 = O.router_logits(PY.to_np(x), PY.to_np(W_g))
+    assert np.abs(PY.to_np(logits) - l64).max() <= 1e-5 * (1 + np.abs(l64).max())
+    ref_idx = O.topk_select(l64, 2)
+    PY.check_routing(idx.cpu().numpy(), wt.cpu().numpy(), ref_idx, O.gate_weights(l64, ref_idx),
+                     l64, 2)
+
+
+def test_router_ties_lower_index_wins(dev):
+    """Columns 5 and 7 of W_g copy column 2, so logits 2, 5, 7 tie exactly (in
+    fp32 on the GPU and in float64 in the oracle).  Where the distinct logit
+    values around the selection are more than 1e-3 apart, the GPU must make
+    the oracle's choice, which resolves the tie towards the lower index."""
+    w = small(T=512, d=128, d_ff=128, E=8)
+    say("router ties")
+    W_g, _, _, _ = W.expert_weights(w, dev, experts=[])
+    W_g[:, 5] = W_g[:, 2]
+    W_g[:, 7] = W_g[:, 2]
+    x = W.make_x(w, W_g, dev)
+    idx, _ = M.moe_router_topk(x, W_g, 2)
+    torch.cuda.synchronize()
+    l64 = O.router_logits(PY.to_np(x), PY.to_np(W_g))
+    assert np.array_equal(l64[:, 2], l64[:, 5]) and np.array_equal(l64[:, 2], l64[:, 7])
+    distinct = -np.sort(-l64[:, [0, 1, 2, 3, 4, 6]], axis=1)
+    ok = (distinct[:, 0] - distinct[:, 1] > 1e-3) & (distinct[:, 1] - distinct[:, 2] > 1e-3)
+    ref = O.topk_select(l64, 2)
+    got = idx.cpu().numpy()
+    assert np.array_equal(got[ok], ref[ok])
+    both = ok & (ref[:, 0] == 2) & (ref[:, 1] == 5)          # tie inside the selection
+    cut = ok & (ref[:, 1] == 2)                              # tie straddles the cut
+    assert both.any() and cut.any()
+    assert not np.any(got[ok] == 7)
+
+
+# ---------------------------------------------------------------- dispatch
+def random_routing(T, E, K, seed, skew=None):
+    g = torch.Generator().manual_seed(seed)
+    if skew is not None:
+        idx = torch.stack([torch.randperm(E, generator=g)[:K] for _ in range(T)]) if T else \
+            torch.empty((0, K), dtype=torch.int64)
+        idx[:, 0] = skew
+        idx[:, 1:] = torch.where(idx[:, 1:] == skew, (skew + 1) % E, idx[:, 1:])
+        if K > 2:
+            return None
+        return idx
+    if T == 0:
+        return torch.empty((0, K), dtype=torch.int64)
+    scores = torch.rand((T, E), generator=g)
+    return torch.argsort(scores, dim=1)[:, :K]
+
+
+@pytest.mark.parametrize("T,E,K", [(1, 8, 2), (7, 8, 2), (1000, 8, 2), (5000, 8, 2),
+                                   (333, 64, 4), (64, 1, 1), (129, 8, 8), (2048, 16, 1)])
+def test_permute_bit_exact(dev, T, E, K):
+    say("permute", T, E, K)
+    idx = random_routing(T, E, K, seed=T * 131 + E * 7 + K)
+    off, st, pos = M.moe_route_permute(idx.to(torch.int32).to(dev), E)
+    torch.cuda.synchronize()
+    counts, r_off, r_st, r_sr, r_pos = O.route_tables(idx.numpy(), E)
+    assert off.cpu().numpy().tolist() == r_off.tolist()
+    assert st.cpu().numpy().tolist() == r_st.tolist()
+    assert pos.cpu().numpy().tolist() == r_pos.tolist()
+
+
+def test_permute_all_to_one_expert(dev):
+    say("permute skew")
+    idx = random_routing(3000, 8, 2, seed=5, skew=3)
+    off, st, pos = M.moe_route_permute(idx.to(torch.int32).to(dev), 8)
+    torch.cuda.synchronize()
+    _, r_off, r_st, _, r_pos = O.route_tables(idx.numpy(), 8)
+    assert off.cpu().tolist() == r_off.tolist()
+    assert st.cpu().tolist() == r_st.tolist() and pos.cpu().numpy().tolist() == r_pos.tolist()
+
+
+# ---------------------------------------------------------------- layer
+def test_layer_tiny_f32(dev):
+    w = W.WORKLOADS["tiny_f32_T64"]
+    say("layer", w.name)
+    check_layer(W.layer_inputs(w, dev), w.K)
+
+
+@pytest.mark.parametrize("T,d,d_ff", [(300, 256, 384), (24, 384, 256), (1, 256, 128),
+                                      (129, 512, 640), (65, 128, 128), (700, 256, 256)])
+def test_layer_bf16_small(dev, T, d, d_ff):
+    w = small(T=T, d=d, d_ff=d_ff)
+    say("layer bf16", T, d, d_ff)
+    check_layer(W.layer_inputs(w, dev), w.K)
+
+
+@pytest.mark.parametrize("E,K", [(8, 1), (8, 8), (64, 4), (1, 1), (16, 3)])
+def test_layer_bf16_k_and_e(dev, E, K):
+    w = small(T=200, d=256, d_ff=256, E=E, K=K)
+    say("layer E K", E, K)
+    check_layer(W.layer_inputs(w, dev), K)
+
+
+def test_layer_f32_general_sizes(dev):
+    w = small(T=77, d=96, d_ff=200, dtype="f32")
+    say("layer f32 ragged", w.T, w.d, w.d_ff)
+    check_layer(W.layer_inputs(w, dev), 2)
+
+
+def test_layer_skewed_routing_prefill_recipe(dev):
+    w = small(name="prefill_bf16_T4096_zipf", T=1500, d=256, d_ff=256)
+    say("layer zipf small")
+    check_layer(W.layer_inputs(w, dev), 2)
+
+
+def test_empty_batch(dev):
+    w = small(T=4, d=128, d_ff=128)
+    inp = W.layer_inputs(w, dev)
+    inp["x"] = inp["x"][:0]
+    y, _ = run_forward(inp, 2)
+    assert y.shape == (0, 128)
+
+
+def test_deterministic_and_stages_match_forward(dev):
+    w = small(T=640, d=256, d_ff=384)
+    say("determinism")
+    inp = W.layer_inputs(w, dev)
+    y1, v1 = run_forward(inp, 2)
+    y2, v2 = run_forward(inp, 2)
+    assert torch.equal(y1, y2)
+    for k in v1:
+        assert torch.equal(v1[k], v2[k]), k
+    idx, wt = M.moe_router_topk(inp["x"], inp["W_g"], 2)
+    off, st, pos = M.moe_route_permute(idx, w.E)
+    H = M.moe_expert_swiglu(inp["x"], inp["W1"], inp["W3"], 2, off, st)
+    Ob = M.moe_expert_down(H, inp["W2"], w.T, 2, off)
+    y3 = M.moe_combine(Ob, wt, pos)
+    torch.cuda.synchronize()
+    assert torch.equal(y3, y1)
+    assert torch.equal(H, v1["H"]) and torch.equal(Ob, v1["O"])
+
+
+def test_scaling_w2_scales_output_exactly(dev):
+    w = small(T=200, d=256, d_ff=256)
+    inp = W.layer_inputs(w, dev)
+    y, _ = run_forward(inp, 2)
+    inp2 = dict(inp, W2=[2 * t for t in inp["W2"]])
+    y2, _ = run_forward(inp2, 2)
+    assert torch.equal(y2, 2 * y)
+
+
+def test_accumulate_adds_residual_then_rounds(dev):
+    w = small(T=100, d=256, d_ff=256)
+    inp = W.layer_inputs(w, dev)
+    y32, _ = run_forward(inp, 2)
+    h = torch.randn((w.T, w.d), generator=torch.Generator(device=dev).manual_seed(3),
+                    device=dev).to(torch.bfloat16)
+    yacc = h.clone()
+    run_forward(inp, 2, y_dtype=torch.bfloat16, y=yacc, accumulate=True)
+    assert torch.equal(yacc, (h.float() + y32).to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rmsnorm(dev, dtype):
+    g = torch.Generator(device=dev).manual_seed(11)
+    h = (torch.randn((33, 4096), generator=g, device=dev) * 3)
+    h = h.to(torch.bfloat16) if dtype == "bf16" else h
+    out = M.moe_rmsnorm(h)
+    torch.cuda.synchronize()
+    ref = O.rmsnorm(PY.to_np(h), 1e-5)
+    err = np.abs(PY.to_np(out) - ref).max()
+    assert err <= (2.0 ** -7 * np.abs(ref).max() if dtype == "bf16" else 1e-5)
+
+
+# ---------------------------------------------------------------- full size
+def _full(name, dev, tokens, check_perm_all=True):
+    w = W.WORKLOADS[name]
+    say("full size", name)
+    inp = W.layer_inputs(w, dev)
+    y32, v = run_forward(inp, w.K)
+    yb, _ = run_forward(inp, w.K, torch.bfloat16)
+    assert torch.equal(yb, PY.bf16_rne_of(y32))
+    # routing of every token (the router is cheap in float64)
+    l64 = O.router_logits(PY.to_np(inp["x"]), PY.to_np(inp["W_g"]))
+    ref_idx = O.topk_select(l64, w.K)
+    set_ok = PY.check_routing(v["topk_idx"].cpu().numpy(), v["topk_w"].cpu().numpy(), ref_idx,
+                              O.gate_weights(l64, ref_idx), l64, w.K)
+    if check_perm_all:
+        PY.check_permutation(v["offsets"].cpu().numpy(), v["sorted_token"].cpu().numpy(),
+                             ref_idx, w.E, w.K, set_ok)
+    rows = np.asarray(tokens)
+    y_ref, aux = oracle(inp, w.K, faithful=True, tokens=rows)
+    keep = set_ok[rows]
+    err = PY.rel_err(PY.to_np(y32)[rows], y_ref, keep)
+    say("%s: rel err %.3e over %d sampled tokens" % (name, err, keep.sum()))
+    assert err <= PY.TOL_BF16
+    y_exact, _ = oracle(inp, w.K, faithful=False, tokens=rows[:8])
+    say("%s: rel err vs exact (reported) %.3e" % (name, PY.rel_err(PY.to_np(y32)[rows[:8]],
+                                                                   y_exact, keep[:8])))
+
+
+def test_full_decode_T8(dev):
+    _full("decode_bf16_T8", dev, tokens=range(8))
+
+
+def test_full_T512_sampled(dev):
+    _full("mid_bf16_T512", dev, tokens=np.random.default_rng(1).choice(512, 32, replace=False))
+
+
+def test_full_prefill_T4096_sampled(dev):
+    rng = np.random.default_rng(2)
+    _full("prefill_bf16_T4096_zipf", dev, tokens=np.sort(rng.choice(4096, 32, replace=False)))
