@@ -52,8 +52,11 @@ class Layer:
         self.offsets = torch.empty(E + 1, **i32)
         self.sorted_token = torch.empty(P, **i32)
         self.pos = torch.empty((T, K), **i32)
+        self.plan = M.plan_for(T, d, d_ff, E, K, M.BF16)
         self.H = torch.empty((P, d_ff), dtype=torch.bfloat16, device=dev)
-        self.O = torch.empty((P, d), dtype=torch.float32, device=dev)
+        self.O = torch.empty((self.plan["down_splits"], P, d), dtype=torch.float32, device=dev)
+        self.scratch = torch.empty(max(self.plan["swiglu_scratch_bytes"], 16), dtype=torch.uint8,
+                                   device=dev)
         self.y = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
         self.ws = torch.empty(M.workspace_size(T, d, d_ff, E, K, M.BF16), dtype=torch.uint8,
                               device=dev)
@@ -72,7 +75,8 @@ class Layer:
         mark(1)
         M.moe_route_permute(self.topk_idx, w.E, self.offsets, self.sorted_token, self.pos)
         mark(2)
-        M.moe_expert_swiglu(self.x, self.W1, self.W3, w.K, self.offsets, self.sorted_token, self.H)
+        M.moe_expert_swiglu(self.x, self.W1, self.W3, w.K, self.offsets, self.sorted_token, self.H,
+                            self.scratch)
         mark(3)
         M.moe_expert_down(self.H, self.W2, w.T, w.K, self.offsets, self.O)
         mark(4)
@@ -164,12 +168,16 @@ def cpu_baseline(layer: Layer, max_tokens: int = 8):
     W1 = [t.float().cpu().numpy() for t in layer.W1]
     W3 = [t.float().cpu().numpy() for t in layer.W3]
     W2 = [t.float().cpu().numpy() for t in layer.W2]
-    t0 = time.perf_counter()
-    O.moe_forward(x, Wg, W1, W3, W2, w.K, faithful=True)
-    dt = time.perf_counter() - t0
+    reps, t0 = 0, time.perf_counter()
+    while True:        # repeat the sample until ~10 s of CPU work (at least 3 runs)
+        O.moe_forward(x, Wg, W1, W3, W2, w.K, faithful=True)
+        reps += 1
+        if reps >= 3 and time.perf_counter() - t0 >= 10.0:
+            break
+    dt = (time.perf_counter() - t0) / reps
     return dict(value=round(n / dt, 3), unit="tokens/s", cores=int(threads), kind="oracle",
-                sample="first %d of %d tokens of %s, float64 oracle, faithful mode, %.2f s"
-                       % (n, w.T, w.name, dt))
+                sample="first %d of %d tokens of %s, float64 oracle in faithful mode, "
+                       "%.2f s per run, mean of %d runs" % (n, w.T, w.name, dt, reps))
 
 
 def run_workload(name, dev, steps, warmup):
@@ -186,6 +194,7 @@ def run_workload(name, dev, steps, warmup):
                ms_per_step_single_call=round(wall_fwd / steps * 1e3, 4),
                stage_ms={k: round(v, 4) for k, v in per_stage.items()},
                n_active_experts=alg["n_active"], expert_counts=counts.tolist(),
+               plan=layer.plan,
                layer_roofline_frac=round(max(alg["layer_bytes"] / (HBM_PEAK_GBS * 1e9),
                                              alg["layer_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12))
                                          / (ms * 1e-3), 4),

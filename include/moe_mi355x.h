@@ -56,6 +56,17 @@ typedef enum {
   MOE_EHIP = 4           /* a HIP launch reported an error */
 } moe_status;
 
+/*
+ * How moe_forward runs a shape; the stage entry points follow the same plan,
+ * so a caller of the stages runs exactly the kernels moe_forward runs.
+ */
+typedef struct moe_plan {
+  int32_t swiglu_splits;        /* K splits of the W1/W3 product (1 = fused epilogue)   */
+  int32_t down_splits;          /* K splits of the W2 product = slices of O             */
+  size_t swiglu_scratch_bytes;  /* fp32 partial sums the W1/W3 product needs (0 if none) */
+  int32_t streaming;            /* 1: weight-streaming (small batch) kernels, 0: tiled   */
+} moe_plan;
+
 /* Index of each intermediate inside the workspace; see moe_workspace_layout. */
 typedef enum {
   MOE_WS_TOPK_IDX = 0,     /* int32 [T, K]   expert of rank r of token t            */
@@ -64,8 +75,9 @@ typedef enum {
   MOE_WS_SORTED_TOKEN = 3, /* int32 [T*K]    token of each expert-sorted pair       */
   MOE_WS_POS = 4,          /* int32 [T, K]   sorted position of pair (t, r)         */
   MOE_WS_H = 5,            /* dtype [T*K, d_ff]  SwiGLU product, expert-sorted rows */
-  MOE_WS_O = 6,            /* float [T*K, d]     expert outputs, expert-sorted rows */
-  MOE_WS_COUNT = 7
+  MOE_WS_O = 6,            /* float [down_splits, T*K, d]  expert outputs (slices)  */
+  MOE_WS_SCRATCH = 7,      /* swiglu_scratch_bytes of fp32 partial sums             */
+  MOE_WS_COUNT = 8
 } moe_ws_item;
 
 /* Human-readable name of a status. */
@@ -76,6 +88,13 @@ const char* moe_last_error(void);
 
 /* MOE_ABI_VERSION of the loaded library. */
 int32_t moe_abi_version(void);
+
+/*
+ * The plan moe_forward uses for this shape.  Errors: MOE_EINVAL for bad
+ * sizes or a NULL `plan`, MOE_EUNSUPPORTED as moe_forward.
+ */
+moe_status moe_plan_for(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K, int32_t dtype,
+                        moe_plan* plan);
 
 /*
  * Bytes of workspace moe_forward needs for this shape (256-byte aligned
@@ -139,15 +158,20 @@ moe_status moe_route_permute(const int32_t* topk_idx, int64_t T, int32_t E, int3
  * Step 6 (code block D, first line): for every expert-sorted pair row r of
  * expert e, H[r] = round(SiLU(x[sorted_token[r]] W1[e]) * (x[...] W3[e])),
  * fp32 accumulation, one rounding to dtype.  H [T*K, d_ff] in dtype.
+ * scratch: device buffer of plan.swiglu_scratch_bytes (may be NULL when that
+ * is 0); MOE_EWORKSPACE if smaller.  Partial sums over the K splits are added
+ * in split order.
  */
 moe_status moe_expert_swiglu(const void* x, const void* const* W1, const void* const* W3,
                              int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K,
                              int32_t dtype, const int32_t* offsets, const int32_t* sorted_token,
-                             void* H, void* stream);
+                             void* H, void* scratch, size_t scratch_bytes, void* stream);
 
 /*
- * Step 7 (code block D, second line): O[r] = H[r] W2[e] for every sorted row
- * r of expert e, fp32 accumulation, O float [T*K, d].
+ * Step 7 (code block D, second line): O_s[r] = H[r, k-slice s] W2[e][k-slice s]
+ * for every sorted row r of expert e and every split s < plan.down_splits,
+ * fp32 accumulation.  O float [plan.down_splits, T*K, d]; the sum over s is
+ * taken by moe_combine.
  */
 moe_status moe_expert_down(const void* H, const void* const* W2, int64_t T, int64_t d,
                            int64_t d_ff, int32_t E, int32_t K, int32_t dtype,
@@ -155,12 +179,13 @@ moe_status moe_expert_down(const void* H, const void* const* W2, int64_t T, int6
 
 /*
  * Step 8 (section 2.1.1 sum; code block E, zero-initialised accumulator):
- * s = w[t,0]*O[pos[t,0]], then s = fma(w[t,r], O[pos[t,r]], s) for r = 1..K-1
- * in fp32; y[t] = round(s), or round(y[t] + s) when accumulate = 1.
+ * o_r = sum over s < o_splits of O[s][pos[t,r]] (in s order), then
+ * s = w[t,0]*o_0 and s = fma(w[t,r], o_r, s) for r = 1..K-1, in fp32;
+ * y[t] = round(s), or round(y[t] + s) when accumulate = 1.
  */
-moe_status moe_combine(const float* O, const float* topk_w, const int32_t* pos, int64_t T,
-                       int64_t d, int32_t K, void* y, int32_t y_dtype, int32_t accumulate,
-                       void* stream);
+moe_status moe_combine(const float* O, int32_t o_splits, const float* topk_w, const int32_t* pos,
+                       int64_t T, int64_t d, int32_t K, void* y, int32_t y_dtype,
+                       int32_t accumulate, void* stream);
 
 /*
  * Pre-norm glue for a stack of blocks ("【DL輪読会】Mixtral of Experts"

@@ -22,17 +22,17 @@ from .build import library_path
 
 __all__ = [
     "MoeError", "MoeLibraryMissing", "F32", "BF16", "WS_ITEMS",
-    "load_library", "workspace_size", "workspace_layout", "moe_forward",
+    "load_library", "plan_for", "workspace_size", "workspace_layout", "moe_forward",
     "moe_router_topk", "moe_route_permute", "moe_expert_swiglu", "moe_expert_down",
     "moe_combine", "moe_rmsnorm", "EXPORTED_SYMBOLS",
 ]
 
 F32 = 0
 BF16 = 1
-WS_ITEMS = ("topk_idx", "topk_w", "offsets", "sorted_token", "pos", "H", "O")
+WS_ITEMS = ("topk_idx", "topk_w", "offsets", "sorted_token", "pos", "H", "O", "scratch")
 
 EXPORTED_SYMBOLS = (
-    "moe_status_str", "moe_last_error", "moe_abi_version", "moe_workspace_size",
+    "moe_status_str", "moe_last_error", "moe_abi_version", "moe_plan_for", "moe_workspace_size",
     "moe_workspace_layout", "moe_forward", "moe_router_topk", "moe_route_permute",
     "moe_expert_swiglu", "moe_expert_down", "moe_combine", "moe_rmsnorm",
 )
@@ -56,6 +56,11 @@ _c_p = ctypes.c_void_p
 _c_sz = ctypes.c_size_t
 
 
+class _Plan(ctypes.Structure):
+    _fields_ = [("swiglu_splits", ctypes.c_int32), ("down_splits", ctypes.c_int32),
+                ("swiglu_scratch_bytes", ctypes.c_size_t), ("streaming", ctypes.c_int32)]
+
+
 def load_library(path: str | None = None):
     """Load (once) and return the ctypes handle of libmoe_mi355x.so."""
     global _lib
@@ -71,6 +76,8 @@ def load_library(path: str | None = None):
         "moe_status_str": (ctypes.c_char_p, [_c_i32]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_abi_version": (_c_i32, []),
+        "moe_plan_for": (_c_i32, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
+                                  ctypes.POINTER(_Plan)]),
         "moe_workspace_size": (_c_i32, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
                                         ctypes.POINTER(_c_sz)]),
         "moe_workspace_layout": (_c_i32, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
@@ -81,11 +88,11 @@ def load_library(path: str | None = None):
                                      _c_p, _c_p, _c_p]),
         "moe_route_permute": (_c_i32, [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p]),
         "moe_expert_swiglu": (_c_i32, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32,
-                                       _c_i32, _c_p, _c_p, _c_p, _c_p]),
+                                       _c_i32, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
         "moe_expert_down": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
                                      _c_p, _c_p, _c_p]),
-        "moe_combine": (_c_i32, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_i32, _c_i32,
-                                 _c_p]),
+        "moe_combine": (_c_i32, [_c_p, _c_i32, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_i32,
+                                 _c_i32, _c_p]),
         "moe_rmsnorm": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, ctypes.c_float, _c_i32, _c_p]),
     }
     for name, (res, args) in sig.items():
@@ -131,6 +138,15 @@ def _stream(stream=None):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def plan_for(T, d, d_ff, E, K, dtype) -> dict:
+    """The kernel plan moe_forward (and the stage calls) use for a shape."""
+    lib = load_library()
+    p = _Plan()
+    _check(lib.moe_plan_for(T, d, d_ff, E, K, dtype, ctypes.byref(p)), lib)
+    return dict(swiglu_splits=p.swiglu_splits, down_splits=p.down_splits,
+                swiglu_scratch_bytes=p.swiglu_scratch_bytes, streaming=bool(p.streaming))
+
+
 def workspace_size(T, d, d_ff, E, K, dtype) -> int:
     lib = load_library()
     out = _c_sz(0)
@@ -148,6 +164,8 @@ def workspace_layout(T, d, d_ff, E, K, dtype) -> dict:
 def workspace_views(ws: torch.Tensor, T, d, d_ff, E, K, dtype) -> dict:
     """Typed views of the intermediates moe_forward leaves in a workspace."""
     off = workspace_layout(T, d, d_ff, E, K, dtype)
+    plan = plan_for(T, d, d_ff, E, K, dtype)
+    S = plan["down_splits"]
     P = T * K
     hdt = torch.bfloat16 if dtype == BF16 else torch.float32
 
@@ -162,7 +180,7 @@ def workspace_views(ws: torch.Tensor, T, d, d_ff, E, K, dtype) -> dict:
         sorted_token=view("sorted_token", P, torch.int32),
         pos=view("pos", P, torch.int32).view(T, K),
         H=view("H", P * d_ff, hdt).view(P, d_ff),
-        O=view("O", P * d, torch.float32).view(P, d),
+        O=view("O", S * P * d, torch.float32).view(S, P, d),
     )
 
 
@@ -219,38 +237,48 @@ def moe_route_permute(topk_idx, E, offsets=None, sorted_token=None, pos=None, st
     return offsets, sorted_token, pos
 
 
-def moe_expert_swiglu(x, W1, W3, K, offsets, sorted_token, H=None, stream=None):
+def moe_expert_swiglu(x, W1, W3, K, offsets, sorted_token, H=None, scratch=None, stream=None):
     lib = load_library()
     T, d = x.shape
     E = len(W1)
     d_ff = W1[0].shape[1]
+    dt = _dtype_code(x)
     if H is None:
         H = torch.empty((T * K, d_ff), dtype=x.dtype, device=x.device)
-    _check(lib.moe_expert_swiglu(_ptr(x), _ptr_array(W1), _ptr_array(W3), T, d, d_ff, E, K,
-                                 _dtype_code(x), _ptr(offsets), _ptr(sorted_token), _ptr(H),
+    need = plan_for(T, d, d_ff, E, K, dt)["swiglu_scratch_bytes"] if T else 0
+    if scratch is None and need:
+        scratch = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(lib.moe_expert_swiglu(_ptr(x), _ptr_array(W1), _ptr_array(W3), T, d, d_ff, E, K, dt,
+                                 _ptr(offsets), _ptr(sorted_token), _ptr(H), _ptr(scratch),
+                                 scratch.numel() if scratch is not None else 0,
                                  _stream(stream)), lib)
     return H
 
 
 def moe_expert_down(H, W2, T, K, offsets, O=None, stream=None):
+    """O has shape [down_splits, T*K, d] (see plan_for)."""
     lib = load_library()
     E = len(W2)
     d_ff, d = W2[0].shape
+    dt = _dtype_code(H)
     if O is None:
-        O = torch.empty((T * K, d), dtype=torch.float32, device=H.device)
-    _check(lib.moe_expert_down(_ptr(H), _ptr_array(W2), T, d, d_ff, E, K, _dtype_code(H),
+        S = plan_for(T, d, d_ff, E, K, dt)["down_splits"] if T else 1
+        O = torch.empty((S, T * K, d), dtype=torch.float32, device=H.device)
+    _check(lib.moe_expert_down(_ptr(H), _ptr_array(W2), T, d, d_ff, E, K, dt,
                                _ptr(offsets), _ptr(O), _stream(stream)), lib)
     return O
 
 
 def moe_combine(O, topk_w, pos, y=None, y_dtype=torch.float32, accumulate=False, stream=None):
+    """O is [splits, T*K, d] (or [T*K, d] for one split)."""
     lib = load_library()
     T, K = topk_w.shape
-    d = O.shape[1]
+    O3 = O if O.dim() == 3 else O.unsqueeze(0)
+    S, _, d = O3.shape
     if y is None:
         y = torch.empty((T, d), dtype=y_dtype, device=O.device)
-    _check(lib.moe_combine(_ptr(O), _ptr(topk_w), _ptr(pos), T, d, K, _ptr(y), _dtype_code(y),
-                           1 if accumulate else 0, _stream(stream)), lib)
+    _check(lib.moe_combine(_ptr(O3), S, _ptr(topk_w), _ptr(pos), T, d, K, _ptr(y),
+                           _dtype_code(y), 1 if accumulate else 0, _stream(stream)), lib)
     return y
 
 

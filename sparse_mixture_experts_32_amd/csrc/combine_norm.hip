@@ -4,7 +4,8 @@
 // Combine: "从Mistral 7B到MoE模型Mixtral 8x7B的全面解析" (aiqianji.com) section
 // 2.1.1 (y = sum_i G(x)_i E_i(x)) and section 3.2.5 code block E (the output
 // starts from zero and each routed expert output is added).  Here each token
-// gathers its K expert rows O[pos[t, r]] and sums them in rank order in fp32
+// gathers its K expert rows O[pos[t, r]] (each the sum of the K-split slices
+// of the W2 product, added in slice order) and sums them in rank order in fp32
 // with one fixed expression, s = w0*O0, then s = fma(w_r, O_r, s); y is rounded
 // once (after adding the residual in accumulate mode).  No atomics: bitwise
 // reproducible.
@@ -29,9 +30,29 @@ __device__ __forceinline__ float load_y<bf16_t>(const bf16_t* y, int64_t i) {
 __device__ __forceinline__ void store_y(float* y, int64_t i, float v) { y[i] = v; }
 __device__ __forceinline__ void store_y(bf16_t* y, int64_t i, float v) { y[i] = f32_to_bf16(v); }
 
+// Sum of the o_splits slices of O at element i, in slice order.
+__device__ __forceinline__ float4 load_o4(const float* O, int splits, int64_t slice, int64_t i) {
+  float4 v = *reinterpret_cast<const float4*>(O + i);
+  for (int s = 1; s < splits; ++s) {
+    const float4 u = *reinterpret_cast<const float4*>(O + s * slice + i);
+    v.x += u.x;
+    v.y += u.y;
+    v.z += u.z;
+    v.w += u.w;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float load_o1(const float* O, int splits, int64_t slice, int64_t i) {
+  float v = O[i];
+  for (int s = 1; s < splits; ++s) v += O[s * slice + i];
+  return v;
+}
+
 // One thread per 4 consecutive features of one token (d % 4 == 0).
 template <typename YT, bool ACC>
-__global__ __launch_bounds__(256) void combine_vec4_kernel(const float* __restrict__ O,
+__global__ __launch_bounds__(256) void combine_vec4_kernel(const float* __restrict__ O, int splits,
+                                                           int64_t slice,
                                                            const float* __restrict__ topk_w,
                                                            const int32_t* __restrict__ pos, int T,
                                                            int d, int K, YT* __restrict__ y) {
@@ -42,11 +63,11 @@ __global__ __launch_bounds__(256) void combine_vec4_kernel(const float* __restri
     const int c = (int)(g % (d / 4)) * 4;
     const float* wt = topk_w + (int64_t)t * K;
     const int32_t* pt = pos + (int64_t)t * K;
-    const float4 o0 = *reinterpret_cast<const float4*>(O + (int64_t)pt[0] * d + c);
+    const float4 o0 = load_o4(O, splits, slice, (int64_t)pt[0] * d + c);
     const float w0 = wt[0];
     float s0 = w0 * o0.x, s1 = w0 * o0.y, s2 = w0 * o0.z, s3 = w0 * o0.w;
     for (int r = 1; r < K; ++r) {
-      const float4 o = *reinterpret_cast<const float4*>(O + (int64_t)pt[r] * d + c);
+      const float4 o = load_o4(O, splits, slice, (int64_t)pt[r] * d + c);
       const float w = wt[r];
       s0 = fmaf(w, o.x, s0);
       s1 = fmaf(w, o.y, s1);
@@ -74,6 +95,7 @@ __global__ __launch_bounds__(256) void combine_vec4_kernel(const float* __restri
 // Scalar fallback for any d.
 template <typename YT, bool ACC>
 __global__ __launch_bounds__(256) void combine_scalar_kernel(const float* __restrict__ O,
+                                                             int splits, int64_t slice,
                                                              const float* __restrict__ topk_w,
                                                              const int32_t* __restrict__ pos,
                                                              int T, int d, int K,
@@ -85,27 +107,27 @@ __global__ __launch_bounds__(256) void combine_scalar_kernel(const float* __rest
     const int c = (int)(g % d);
     const float* wt = topk_w + (int64_t)t * K;
     const int32_t* pt = pos + (int64_t)t * K;
-    float s = wt[0] * O[(int64_t)pt[0] * d + c];
-    for (int r = 1; r < K; ++r) s = fmaf(wt[r], O[(int64_t)pt[r] * d + c], s);
+    float s = wt[0] * load_o1(O, splits, slice, (int64_t)pt[0] * d + c);
+    for (int r = 1; r < K; ++r) s = fmaf(wt[r], load_o1(O, splits, slice, (int64_t)pt[r] * d + c), s);
     if (ACC) s = load_y(y, g) + s;
     store_y(y, g, s);
   }
 }
 
 template <typename YT, bool ACC>
-hipError_t launch_combine_t(const float* O, const float* w, const int32_t* pos, int T, int d,
-                            int K, void* y, hipStream_t stream) {
+hipError_t launch_combine_t(const float* O, int splits, int64_t slice, const float* w,
+                            const int32_t* pos, int T, int d, int K, void* y, hipStream_t stream) {
   const int threads = 256;
   if (d % 4 == 0) {
     const int64_t groups = (int64_t)T * (d / 4);
     const int blocks = (int)std::min<int64_t>((groups + threads - 1) / threads, 4096);
     hipLaunchKernelGGL((combine_vec4_kernel<YT, ACC>), dim3(blocks), dim3(threads), 0, stream, O,
-                       w, pos, T, d, K, static_cast<YT*>(y));
+                       splits, slice, w, pos, T, d, K, static_cast<YT*>(y));
   } else {
     const int64_t n = (int64_t)T * d;
     const int blocks = (int)std::min<int64_t>((n + threads - 1) / threads, 4096);
     hipLaunchKernelGGL((combine_scalar_kernel<YT, ACC>), dim3(blocks), dim3(threads), 0, stream,
-                       O, w, pos, T, d, K, static_cast<YT*>(y));
+                       O, splits, slice, w, pos, T, d, K, static_cast<YT*>(y));
   }
   return hipGetLastError();
 }
@@ -134,13 +156,17 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ h, T
 
 }  // namespace
 
-hipError_t launch_combine(const float* O, const float* topk_w, const int32_t* pos, int T, int d,
-                          int K, void* y, int y_dtype, int accumulate, hipStream_t stream) {
+hipError_t launch_combine(const float* O, int o_splits, int64_t slice, const float* topk_w,
+                          const int32_t* pos, int T, int d, int K, void* y, int y_dtype,
+                          int accumulate, hipStream_t stream) {
   if (y_dtype == kBF16)
-    return accumulate ? launch_combine_t<bf16_t, true>(O, topk_w, pos, T, d, K, y, stream)
-                      : launch_combine_t<bf16_t, false>(O, topk_w, pos, T, d, K, y, stream);
-  return accumulate ? launch_combine_t<float, true>(O, topk_w, pos, T, d, K, y, stream)
-                    : launch_combine_t<float, false>(O, topk_w, pos, T, d, K, y, stream);
+    return accumulate
+               ? launch_combine_t<bf16_t, true>(O, o_splits, slice, topk_w, pos, T, d, K, y, stream)
+               : launch_combine_t<bf16_t, false>(O, o_splits, slice, topk_w, pos, T, d, K, y,
+                                                 stream);
+  return accumulate
+             ? launch_combine_t<float, true>(O, o_splits, slice, topk_w, pos, T, d, K, y, stream)
+             : launch_combine_t<float, false>(O, o_splits, slice, topk_w, pos, T, d, K, y, stream);
 }
 
 hipError_t launch_rmsnorm(const void* h, void* out, int T, int d, float eps, int dtype,

@@ -66,9 +66,48 @@ moe_status check_shape(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K,
   return MOE_OK;
 }
 
+struct Plan {
+  int swiglu_splits = 1;
+  int down_splits = 1;
+  size_t scratch = 0;
+  bool streaming = false;
+};
+
+// Smallest K split that gives the grid at least ~8 workgroups per compute
+// unit, keeping >= 4 k-steps of 32 per wavefront.
+int choose_splits(int64_t Kdim, int64_t base_blocks) {
+  int best = 1;
+  for (int s = 1; s <= 64; ++s) {
+    if (!moe::stream_gemm_supported((int)Kdim, 128, s)) continue;
+    if (Kdim / (s * 4) < 128) break;
+    best = s;
+    if (base_blocks * s >= 2048) break;
+  }
+  return best;
+}
+
+// Batches whose expert segments fit one 16-row token tile per expert in the
+// common case (T*K <= 64) stream the weights; larger ones use the LDS-tiled
+// matrix-core kernels.
+Plan make_plan(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K, int32_t dt) {
+  Plan p;
+  const int64_t P = T * K;
+  if (dt != MOE_BF16 || P > 64 || P == 0) return p;
+  if (!moe::stream_gemm_supported((int)d, (int)d_ff, 1) ||
+      !moe::stream_gemm_supported((int)d_ff, (int)d, 1))
+    return p;
+  p.streaming = true;
+  const int64_t max_tiles = (P + (int64_t)E * 15) / 16;
+  p.swiglu_splits = choose_splits(d, max_tiles * (d_ff / 128));
+  p.down_splits = choose_splits(d_ff, max_tiles * (d / 128));
+  if (p.swiglu_splits > 1) p.scratch = (size_t)p.swiglu_splits * 2 * P * d_ff * sizeof(float);
+  return p;
+}
+
 void layout(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K, int32_t dt,
             size_t off[MOE_WS_COUNT], size_t* total) {
   const size_t P = (size_t)T * K;
+  const Plan plan = make_plan(T, d, d_ff, E, K, dt);
   size_t o = 0;
   auto put = [&](int item, size_t bytes) {
     off[item] = o;
@@ -80,7 +119,8 @@ void layout(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K, int32_t dt
   put(MOE_WS_SORTED_TOKEN, P * 4);
   put(MOE_WS_POS, P * 4);
   put(MOE_WS_H, P * (size_t)d_ff * dtype_bytes(dt));
-  put(MOE_WS_O, P * (size_t)d * 4);
+  put(MOE_WS_O, (size_t)plan.down_splits * P * (size_t)d * 4);
+  put(MOE_WS_SCRATCH, plan.scratch);
   *total = o;
 }
 
@@ -139,6 +179,19 @@ const char* moe_last_error(void) { return g_err; }
 
 int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
 
+moe_status moe_plan_for(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K, int32_t dtype,
+                        moe_plan* plan) {
+  if (!plan) return fail(MOE_EINVAL, "plan is NULL");
+  moe_status s = check_shape(T, d, d_ff, E, K, dtype);
+  if (s) return s;
+  const Plan p = make_plan(T, d, d_ff, E, K, dtype);
+  plan->swiglu_splits = p.swiglu_splits;
+  plan->down_splits = p.down_splits;
+  plan->swiglu_scratch_bytes = p.scratch;
+  plan->streaming = p.streaming ? 1 : 0;
+  return ok();
+}
+
 moe_status moe_workspace_size(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K,
                               int32_t dtype, size_t* bytes) {
   if (!bytes) return fail(MOE_EINVAL, "bytes is NULL");
@@ -187,10 +240,39 @@ moe_status moe_route_permute(const int32_t* topk_idx, int64_t T, int32_t E, int3
                     "route_permute");
 }
 
+}  // extern "C"
+
+namespace {
+
+hipError_t run_swiglu(const Plan& plan, const void* x, const int32_t* sorted_token,
+                      const moe::ExpertPtrs& p1, const moe::ExpertPtrs& p3, const int32_t* offsets,
+                      int P, int d, int d_ff, int E, int32_t dtype, void* H, void* scratch,
+                      hipStream_t st) {
+  if (dtype != MOE_BF16)
+    return moe::launch_expert_swiglu_f32(x, sorted_token, p1, p3, offsets, P, d, d_ff, E, H, st);
+  if (plan.streaming)
+    return moe::launch_stream_swiglu_bf16(x, sorted_token, p1, p3, offsets, P, d, d_ff, E,
+                                          plan.swiglu_splits, static_cast<float*>(scratch), H, st);
+  return moe::launch_expert_swiglu_bf16(x, sorted_token, p1, p3, offsets, P, d, d_ff, E, H, st);
+}
+
+hipError_t run_down(const Plan& plan, const void* H, const moe::ExpertPtrs& p2,
+                    const int32_t* offsets, int P, int d, int d_ff, int E, int32_t dtype, float* O,
+                    hipStream_t st) {
+  if (dtype != MOE_BF16) return moe::launch_expert_down_f32(H, p2, offsets, P, d, d_ff, E, O, st);
+  if (plan.streaming)
+    return moe::launch_stream_down_bf16(H, p2, offsets, P, d, d_ff, E, plan.down_splits, O, st);
+  return moe::launch_expert_down_bf16(H, p2, offsets, P, d, d_ff, E, O, st);
+}
+
+}  // namespace
+
+extern "C" {
+
 moe_status moe_expert_swiglu(const void* x, const void* const* W1, const void* const* W3,
                              int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K,
                              int32_t dtype, const int32_t* offsets, const int32_t* sorted_token,
-                             void* H, void* stream) {
+                             void* H, void* scratch, size_t scratch_bytes, void* stream) {
   moe_status s = check_shape(T, d, d_ff, E, K, dtype);
   if (s) return s;
   if (T == 0) return ok();
@@ -201,12 +283,16 @@ moe_status moe_expert_swiglu(const void* x, const void* const* W1, const void* c
   moe::ExpertPtrs p1, p3;
   if ((s = fill_ptrs(W1, E, p1, "W1", bf16))) return s;
   if ((s = fill_ptrs(W3, E, p3, "W3", bf16))) return s;
-  const int P = (int)(T * K);
-  hipError_t e = bf16 ? moe::launch_expert_swiglu_bf16(x, sorted_token, p1, p3, offsets, P, (int)d,
-                                                       (int)d_ff, E, H, (hipStream_t)stream)
-                      : moe::launch_expert_swiglu_f32(x, sorted_token, p1, p3, offsets, P, (int)d,
-                                                      (int)d_ff, E, H, (hipStream_t)stream);
-  return finish(e, "expert_swiglu");
+  const Plan plan = make_plan(T, d, d_ff, E, K, dtype);
+  if (plan.scratch > 0) {
+    if (!scratch || scratch_bytes < plan.scratch)
+      return fail(MOE_EWORKSPACE, "scratch has %zu bytes, needs %zu", scratch ? scratch_bytes : 0,
+                  plan.scratch);
+    if (!aligned16(scratch)) return fail(MOE_EWORKSPACE, "scratch must be 16-byte aligned");
+  }
+  return finish(run_swiglu(plan, x, sorted_token, p1, p3, offsets, (int)(T * K), (int)d,
+                           (int)d_ff, E, dtype, H, scratch, (hipStream_t)stream),
+                "expert_swiglu");
 }
 
 moe_status moe_expert_down(const void* H, const void* const* W2, int64_t T, int64_t d,
@@ -221,28 +307,27 @@ moe_status moe_expert_down(const void* H, const void* const* W2, int64_t T, int6
     return fail(MOE_EUNSUPPORTED, "H and O must be 16-byte aligned");
   moe::ExpertPtrs p2;
   if ((s = fill_ptrs(W2, E, p2, "W2", bf16))) return s;
-  const int P = (int)(T * K);
-  hipError_t e = bf16 ? moe::launch_expert_down_bf16(H, p2, offsets, P, (int)d, (int)d_ff, E, O,
-                                                     (hipStream_t)stream)
-                      : moe::launch_expert_down_f32(H, p2, offsets, P, (int)d, (int)d_ff, E, O,
-                                                    (hipStream_t)stream);
-  return finish(e, "expert_down");
+  const Plan plan = make_plan(T, d, d_ff, E, K, dtype);
+  return finish(run_down(plan, H, p2, offsets, (int)(T * K), (int)d, (int)d_ff, E, dtype, O,
+                         (hipStream_t)stream),
+                "expert_down");
 }
 
-moe_status moe_combine(const float* O, const float* topk_w, const int32_t* pos, int64_t T,
-                       int64_t d, int32_t K, void* y, int32_t y_dtype, int32_t accumulate,
-                       void* stream) {
+moe_status moe_combine(const float* O, int32_t o_splits, const float* topk_w, const int32_t* pos,
+                       int64_t T, int64_t d, int32_t K, void* y, int32_t y_dtype,
+                       int32_t accumulate, void* stream) {
   moe_status s = check_dtype(y_dtype, "y_dtype");
   if (s) return s;
   if (T < 0 || d <= 0 || d >= (int64_t(1) << 31) || K < 1 || K > MOE_MAX_EXPERTS)
     return fail(MOE_EINVAL, "bad T, d or K");
+  if (o_splits < 1 || o_splits > 64) return fail(MOE_EINVAL, "o_splits outside [1, 64]");
   if (T == 0) return ok();
   if (!O || !topk_w || !pos || !y) return fail(MOE_EINVAL, "NULL pointer");
   if (d % 4 == 0 && (!aligned16(O) || (y_dtype == MOE_F32 ? !aligned16(y) : ((uintptr_t)y & 7))))
     return fail(MOE_EUNSUPPORTED, "O must be 16-byte and y vector aligned");
-  return finish(moe::launch_combine(O, topk_w, pos, (int)T, (int)d, K, y, y_dtype,
-                                        accumulate ? 1 : 0, (hipStream_t)stream),
-                    "combine");
+  return finish(moe::launch_combine(O, o_splits, T * K * d, topk_w, pos, (int)T, (int)d, K, y,
+                                    y_dtype, accumulate ? 1 : 0, (hipStream_t)stream),
+                "combine");
 }
 
 moe_status moe_rmsnorm(const void* h, void* out, int64_t T, int64_t d, float eps, int32_t dtype,
@@ -299,23 +384,23 @@ moe_status moe_forward(const void* x, const void* W_g, const void* const* W1,
   int32_t* pos = reinterpret_cast<int32_t*>(ws + off[MOE_WS_POS]);
   void* H = ws + off[MOE_WS_H];
   float* O = reinterpret_cast<float*>(ws + off[MOE_WS_O]);
+  void* scratch = ws + off[MOE_WS_SCRATCH];
   hipStream_t st = (hipStream_t)stream;
   const int P = (int)(T * K);
+  const Plan plan = make_plan(T, d, d_ff, E, K, dtype);
 
   hipError_t e = moe::launch_router_topk(x, W_g, (int)T, (int)d, E, K, dtype, topk_idx, topk_w,
                                          nullptr, st);
   if (e != hipSuccess) return hip_status(e, "router_topk");
   e = moe::launch_route_permute(topk_idx, (int)T, E, K, offsets, sorted_token, pos, st);
   if (e != hipSuccess) return hip_status(e, "route_permute");
-  e = bf16 ? moe::launch_expert_swiglu_bf16(x, sorted_token, p1, p3, offsets, P, (int)d,
-                                            (int)d_ff, E, H, st)
-           : moe::launch_expert_swiglu_f32(x, sorted_token, p1, p3, offsets, P, (int)d, (int)d_ff,
-                                           E, H, st);
+  e = run_swiglu(plan, x, sorted_token, p1, p3, offsets, P, (int)d, (int)d_ff, E, dtype, H,
+                 scratch, st);
   if (e != hipSuccess) return hip_status(e, "expert_swiglu");
-  e = bf16 ? moe::launch_expert_down_bf16(H, p2, offsets, P, (int)d, (int)d_ff, E, O, st)
-           : moe::launch_expert_down_f32(H, p2, offsets, P, (int)d, (int)d_ff, E, O, st);
+  e = run_down(plan, H, p2, offsets, P, (int)d, (int)d_ff, E, dtype, O, st);
   if (e != hipSuccess) return hip_status(e, "expert_down");
-  e = moe::launch_combine(O, topk_w, pos, (int)T, (int)d, K, y, y_dtype, accumulate ? 1 : 0, st);
+  e = moe::launch_combine(O, plan.down_splits, (int64_t)P * d, topk_w, pos, (int)T, (int)d, K, y,
+                          y_dtype, accumulate ? 1 : 0, st);
   if (e != hipSuccess) return hip_status(e, "combine");
   return ok();
 }

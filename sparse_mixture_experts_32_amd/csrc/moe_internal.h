@@ -36,12 +36,26 @@ hipError_t launch_expert_down_bf16(const void* H, const ExpertPtrs& W2, const in
 hipError_t launch_expert_down_f32(const void* H, const ExpertPtrs& W2, const int32_t* offsets,
                                   int P, int d, int d_ff, int E, float* O, hipStream_t stream);
 
+// Weight-streaming variants for small batches (every expert segment of at
+// most 16 rows per token tile); K split over `splits` workgroups.
+bool stream_gemm_supported(int Kdim, int N, int splits);
+hipError_t launch_stream_swiglu_bf16(const void* x, const int32_t* sorted_token,
+                                     const ExpertPtrs& W1, const ExpertPtrs& W3,
+                                     const int32_t* offsets, int P, int d, int d_ff, int E,
+                                     int splits, float* part, void* H, hipStream_t stream);
+hipError_t launch_stream_down_bf16(const void* H, const ExpertPtrs& W2, const int32_t* offsets,
+                                   int P, int d, int d_ff, int E, int splits, float* O,
+                                   hipStream_t stream);
+
 // Lets `kernel` use `bytes` of dynamic LDS on the current device (once per
 // device and kernel).
 hipError_t allow_dynamic_lds(const void* kernel, int bytes);
 
-hipError_t launch_combine(const float* O, const float* topk_w, const int32_t* pos, int T, int d,
-                          int K, void* y, int y_dtype, int accumulate, hipStream_t stream);
+// O holds o_splits slices of [P, d]; each token sums its K rows in rank order
+// after summing the slices in slice order.
+hipError_t launch_combine(const float* O, int o_splits, int64_t slice, const float* topk_w,
+                          const int32_t* pos, int T, int d, int K, void* y, int y_dtype,
+                          int accumulate, hipStream_t stream);
 
 hipError_t launch_rmsnorm(const void* h, void* out, int T, int d, float eps, int dtype,
                           hipStream_t stream);

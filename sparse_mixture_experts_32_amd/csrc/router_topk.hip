@@ -1,14 +1,18 @@
-// Router GEMV + top-K + softmax over the selected logits, one wavefront per
-// token ("从Mistral 7B到MoE模型Mixtral 8x7B的全面解析" (aiqianji.com) section
-// 2.1.4: the router is a bias-free linear layer to num_experts scores; section
-// 2.1.1: G(x) = Softmax(TopK(x W_g)), TopK masks every logit outside the K
-// largest to -inf).
+// Router GEMV + top-K + softmax over the selected logits
+// ("从Mistral 7B到MoE模型Mixtral 8x7B的全面解析" (aiqianji.com) section 2.1.4:
+// the router is a bias-free linear layer to num_experts scores; section 2.1.1:
+// G(x) = Softmax(TopK(x W_g)), TopK masks every logit outside the K largest
+// to -inf, so the softmax runs over the K selected logits only).
 //
-// Each lane accumulates a strided slice of the dot products in fp32, a
-// butterfly over the 64 lanes finishes them (fixed order: deterministic).
-// Selection takes K rounds of a wave-wide arg-max with key (-logit, index),
-// so equal logits go to the lower expert index.  The softmax over the K
-// selected logits is exp(l_r - l_0) / sum_s exp(l_s - l_0).
+// TPT threads per token (64 or 256).  Each thread accumulates fp32 partial
+// logits over a strided set of 8-wide k chunks; partials are combined by a
+// butterfly inside each wavefront and then across the token's wavefronts in
+// wave order (fixed order: deterministic).  In the vector path (bf16,
+// E % 8 == 0, d % 8 == 0) a chunk is one 16-byte load of x and eight 16-byte
+// loads of the matching W_g rows.  Selection takes K rounds of a wave-wide
+// arg-max with key (-logit, index), so equal logits go to the lower index.
+// The gate weights are exp(l_r - l_0) / sum_s exp(l_s - l_0) over the K
+// selected, in rank order.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -36,36 +40,80 @@ __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib)
   return (ia >= 0) && (ib < 0 || va > vb || (va == vb && ia < ib));
 }
 
-template <typename T>
+__device__ __forceinline__ void bf16x8_to_f32(const uint4& v, float f[8]) {
+  f[0] = __uint_as_float(v.x << 16);
+  f[1] = __uint_as_float(v.x & 0xffff0000u);
+  f[2] = __uint_as_float(v.y << 16);
+  f[3] = __uint_as_float(v.y & 0xffff0000u);
+  f[4] = __uint_as_float(v.z << 16);
+  f[5] = __uint_as_float(v.z & 0xffff0000u);
+  f[6] = __uint_as_float(v.w << 16);
+  f[7] = __uint_as_float(v.w & 0xffff0000u);
+}
+
+template <typename T, int TPT, bool VEC>
 __global__ __launch_bounds__(256) void router_topk_kernel(const T* __restrict__ x,
                                                           const T* __restrict__ Wg, int T_,
                                                           int d, int E, int K,
                                                           int32_t* __restrict__ topk_idx,
                                                           float* __restrict__ topk_w,
                                                           float* __restrict__ logits_out) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (t >= T_) return;
-  const T* xr = x + static_cast<int64_t>(t) * d;
+  constexpr int kWavesPerTok = TPT / 64;
+  __shared__ float wave_part[256 / 64][kMaxExperts];
+  __shared__ float logit_sh[256 / TPT][kMaxExperts];
 
-  float my_logit = 0.0f;  // lane e keeps logit e (e < E)
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int tok_local = threadIdx.x / TPT;
+  const int sub = threadIdx.x % TPT;          // thread index inside the token's group
+  const int wave_in_tok = sub >> 6;
+  const int t = blockIdx.x * (256 / TPT) + tok_local;
+  const bool live = t < T_;
+  const T* xr = x + static_cast<int64_t>(live ? t : 0) * d;
+
   for (int e0 = 0; e0 < E; e0 += 8) {
     float acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-    for (int k = lane; k < d; k += 64) {
-      const float xv = load_f(xr, k);
-      const T* wrow = Wg + static_cast<int64_t>(k) * E + e0;
+    if (live) {
+      if constexpr (VEC) {
+        for (int k0 = sub * 8; k0 < d; k0 += TPT * 8) {
+          float xv[8];
+          bf16x8_to_f32(*reinterpret_cast<const uint4*>(xr + k0), xv);
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (e0 + j < E) acc[j] = fmaf(xv, load_f(wrow, j), acc[j]);
+          for (int i = 0; i < 8; ++i) {
+            float wv[8];
+            bf16x8_to_f32(*reinterpret_cast<const uint4*>(Wg + (int64_t)(k0 + i) * E + e0), wv);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] = fmaf(xv[i], wv[j], acc[j]);
+          }
+        }
+      } else {
+        for (int k = sub; k < d; k += TPT) {
+          const float xv = load_f(xr, k);
+          const T* wrow = Wg + static_cast<int64_t>(k) * E + e0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (e0 + j < E) acc[j] = fmaf(xv, load_f(wrow, j), acc[j]);
+        }
+      }
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float s = wave_sum(acc[j]);
-      if (lane == e0 + j) my_logit = s;
+      if (lane == 0 && e0 + j < E) wave_part[wave][e0 + j] = s;
     }
   }
+  __syncthreads();
+  // Combine the token's waves in order; lane e of the token's first wave keeps logit e.
+  if (wave_in_tok == 0 && lane < E) {
+    float v = 0.0f;
+    for (int w = 0; w < kWavesPerTok; ++w) v += wave_part[wave + w][lane];
+    logit_sh[tok_local][lane] = v;
+  }
+  __syncthreads();
+  if (!live || wave_in_tok != 0) return;
+  const float my_logit = lane < E ? logit_sh[tok_local][lane] : 0.0f;
   if (logits_out && lane < E) logits_out[static_cast<int64_t>(t) * E + lane] = my_logit;
 
   // K rounds of wave arg-max; lane 0 writes rank r as soon as it is known
@@ -99,22 +147,37 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const T* __restrict__ 
     for (int r = 0; r < K; ++r) out_w[r] = out_w[r] / denom;
 }
 
+template <typename T, int TPT, bool VEC>
+void launch_t(const void* x, const void* Wg, int T_, int d, int E, int K, int32_t* idx,
+              float* w, float* logits, hipStream_t stream) {
+  const int per_block = 256 / TPT;
+  hipLaunchKernelGGL((router_topk_kernel<T, TPT, VEC>), dim3((T_ + per_block - 1) / per_block),
+                     dim3(256), 0, stream, static_cast<const T*>(x), static_cast<const T*>(Wg), T_,
+                     d, E, K, idx, w, logits);
+}
+
 }  // namespace
 
 hipError_t launch_router_topk(const void* x, const void* Wg, int T, int d, int E, int K,
                               int dtype, int32_t* topk_idx, float* topk_w, float* logits,
                               hipStream_t stream) {
-  const int tokens_per_block = 4;
-  dim3 grid((T + tokens_per_block - 1) / tokens_per_block);
-  dim3 block(64 * tokens_per_block);
-  if (dtype == kBF16)
-    hipLaunchKernelGGL(router_topk_kernel<bf16_t>, grid, block, 0, stream,
-                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(Wg), T, d, E, K,
-                       topk_idx, topk_w, logits);
-  else
-    hipLaunchKernelGGL(router_topk_kernel<float>, grid, block, 0, stream,
-                       static_cast<const float*>(x), static_cast<const float*>(Wg), T, d, E, K,
-                       topk_idx, topk_w, logits);
+  // Few tokens: four wavefronts per token; many tokens: one.
+  const bool wide = T < 1024;
+  const bool vec = dtype == kBF16 && E % 8 == 0 && d % 8 == 0 &&
+                   (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(Wg) & 15) == 0;
+  if (dtype == kBF16) {
+    if (vec) {
+      if (wide) launch_t<bf16_t, 256, true>(x, Wg, T, d, E, K, topk_idx, topk_w, logits, stream);
+      else launch_t<bf16_t, 64, true>(x, Wg, T, d, E, K, topk_idx, topk_w, logits, stream);
+    } else {
+      if (wide) launch_t<bf16_t, 256, false>(x, Wg, T, d, E, K, topk_idx, topk_w, logits, stream);
+      else launch_t<bf16_t, 64, false>(x, Wg, T, d, E, K, topk_idx, topk_w, logits, stream);
+    }
+  } else {
+    if (wide) launch_t<float, 256, false>(x, Wg, T, d, E, K, topk_idx, topk_w, logits, stream);
+    else launch_t<float, 64, false>(x, Wg, T, d, E, K, topk_idx, topk_w, logits, stream);
+  }
   return hipGetLastError();
 }
 

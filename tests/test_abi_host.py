@@ -53,6 +53,16 @@ def test_version_and_status_strings(lib):
     assert lib.moe_status_str(4) == b"MOE_EHIP"
 
 
+def test_plan(lib):
+    p = M.plan_for(8, 4096, 14336, 8, 2, M.BF16)
+    assert p["streaming"] and p["swiglu_splits"] > 1 and p["down_splits"] > 1
+    assert p["swiglu_scratch_bytes"] == p["swiglu_splits"] * 2 * 16 * 14336 * 4
+    p = M.plan_for(4096, 4096, 14336, 8, 2, M.BF16)
+    assert not p["streaming"] and p["swiglu_splits"] == 1 and p["down_splits"] == 1
+    p = M.plan_for(8, 128, 256, 8, 2, M.F32)
+    assert not p["streaming"]
+
+
 def test_workspace_size_and_layout(lib):
     n = ctypes.c_size_t()
     assert lib.moe_workspace_size(4096, 4096, 14336, 8, 2, 1, ctypes.byref(n)) == OK
@@ -115,12 +125,16 @@ def test_stage_entry_points_validate(lib):
     assert lib.moe_route_permute(FAKE, 4, 65, 2, FAKE, FAKE, FAKE, None) == EINVAL
     assert lib.moe_route_permute(FAKE, 4, 8, 2, None, FAKE, FAKE, None) == EINVAL
     assert lib.moe_expert_swiglu(FAKE, arr, arr, 4, 100, 256, 8, 2, 1, FAKE, FAKE, FAKE,
-                                 None) == EUNSUPPORTED
+                                 None, 0, None) == EUNSUPPORTED
     assert lib.moe_expert_swiglu(FAKE, arr, arr, 4, 128, 256, 8, 2, 1, None, FAKE, FAKE,
-                                 None) == EINVAL
+                                 None, 0, None) == EINVAL
+    # the streaming plan of an 8-token Mixtral-shape layer needs scratch
+    assert lib.moe_expert_swiglu(FAKE, arr, arr, 8, 4096, 14336, 8, 2, 1, FAKE, FAKE, FAKE,
+                                 None, 0, None) == EWORKSPACE
     assert lib.moe_expert_down(FAKE, arr, 4, 128, 256, 8, 2, 1, FAKE, None, None) == EINVAL
-    assert lib.moe_combine(FAKE, FAKE, FAKE, 4, 128, 0, FAKE2, 0, 0, None) == EINVAL
-    assert lib.moe_combine(FAKE, FAKE, FAKE, 4, 128, 2, None, 0, 0, None) == EINVAL
+    assert lib.moe_combine(FAKE, 1, FAKE, FAKE, 4, 128, 0, FAKE2, 0, 0, None) == EINVAL
+    assert lib.moe_combine(FAKE, 1, FAKE, FAKE, 4, 128, 2, None, 0, 0, None) == EINVAL
+    assert lib.moe_combine(FAKE, 0, FAKE, FAKE, 4, 128, 2, FAKE2, 0, 0, None) == EINVAL
     assert lib.moe_rmsnorm(FAKE, FAKE, 4, 128, 1e-5, 1, None) == EINVAL     # overlap
     assert lib.moe_rmsnorm(FAKE, FAKE2, 4, 128, -1.0, 1, None) == EINVAL
     for fn_args in [(FAKE, FAKE, 0, 64, 8, 2, 1, FAKE, FAKE, None, None)]:

@@ -196,6 +196,18 @@ def test_layer_bf16_small(dev, T, d, d_ff):
     check_layer(W.layer_inputs(w, dev), w.K)
 
 
+@pytest.mark.parametrize("T,d,d_ff", [(8, 2048, 1024), (3, 1024, 2048), (32, 512, 1536),
+                                      (8, 1024, 512), (1, 1024, 1024)])
+def test_layer_bf16_streaming_splits(dev, T, d, d_ff):
+    """Small batches take the weight-streaming kernels with K split over
+    workgroups (partial sums added in split order)."""
+    w = small(T=T, d=d, d_ff=d_ff)
+    plan = M.plan_for(T, d, d_ff, w.E, w.K, M.BF16)
+    say("layer streaming", T, d, d_ff, plan)
+    assert plan["streaming"]
+    check_layer(W.layer_inputs(w, dev), w.K)
+
+
 @pytest.mark.parametrize("E,K", [(8, 1), (8, 8), (64, 4), (1, 1), (16, 3)])
 def test_layer_bf16_k_and_e(dev, E, K):
     w = small(T=200, d=256, d_ff=256, E=E, K=K)
