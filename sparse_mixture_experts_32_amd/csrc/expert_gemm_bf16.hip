@@ -52,115 +52,121 @@ __device__ __forceinline__ uint32_t perm_hi(uint32_t hi_src, uint32_t lo_src) {
   return __builtin_amdgcn_perm(hi_src, lo_src, 0x07060302u);
 }
 
-__device__ __forceinline__ uint32_t comp(const uint4& v, int q) {
-  return q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
-}
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // rows[r] holds 8 bf16 of row r (columns c = 0..7, two per dword); on return
 // cols[c] holds 8 bf16 of column c (rows r = 0..7).
-__device__ __forceinline__ void transpose8x8(const uint4 rows[8], uint4 cols[8]) {
+__device__ __forceinline__ void transpose8x8(const u32x4_t rows[8], u32x4_t cols[8]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    cols[2 * q] = make_uint4(perm_lo(comp(rows[1], q), comp(rows[0], q)),
-                             perm_lo(comp(rows[3], q), comp(rows[2], q)),
-                             perm_lo(comp(rows[5], q), comp(rows[4], q)),
-                             perm_lo(comp(rows[7], q), comp(rows[6], q)));
-    cols[2 * q + 1] = make_uint4(perm_hi(comp(rows[1], q), comp(rows[0], q)),
-                                 perm_hi(comp(rows[3], q), comp(rows[2], q)),
-                                 perm_hi(comp(rows[5], q), comp(rows[4], q)),
-                                 perm_hi(comp(rows[7], q), comp(rows[6], q)));
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      cols[2 * q][m] = perm_lo(rows[2 * m + 1][q], rows[2 * m][q]);
+      cols[2 * q + 1][m] = perm_hi(rows[2 * m + 1][q], rows[2 * m][q]);
+    }
   }
 }
 
-template <int BF, int BT, int BK, int WAVES_F, int WAVES_T, bool DUAL>
+// BF weight columns (both matrices together when DUAL: the first BF/2 LDS rows
+// hold W1 features, the last BF/2 the same W3 features) x BT tokens per
+// workgroup, BK reduction depth per stage; four waves in a 2 x 2 grid, each
+// owning (BF/2) x (BT/2).
+template <int BF, int BT, int BK, bool DUAL>
 struct GemmCfg {
-  static constexpr int kThreads = 64 * WAVES_F * WAVES_T;
-  static constexpr int kMats = DUAL ? 2 : 1;
-  static constexpr int kWF = BF / WAVES_F;  // features per wave
-  static constexpr int kWT = BT / WAVES_T;  // tokens per wave
+  static constexpr int kThreads = 256;
+  static constexpr int kWF = BF / 2;        // weight columns per wave
+  static constexpr int kWT = BT / 2;        // tokens per wave
   static constexpr int kMI = kWF / 16;
   static constexpr int kNJ = kWT / 16;
   static constexpr int kStride = BK + 8;    // LDS row stride in bf16 (16-byte pad)
   static constexpr int kKB = BK / 8;        // 8-row blocks along k
-  static constexpr int kWBlocks = kMats * kKB * (BF / 8);
+  static constexpr int kWBlocks = kKB * (BF / 8);
   static constexpr int kWPerThread = (kWBlocks + kThreads - 1) / kThreads;
   static constexpr int kAChunks = BT * kKB;  // 16-byte chunks of the token tile
   static constexpr int kAPerThread = (kAChunks + kThreads - 1) / kThreads;
-  static constexpr int kLdsW = kMats * BF * kStride;
+  static constexpr int kLdsW = BF * kStride;
   static constexpr int kLdsA = BT * kStride;
   static constexpr int kLdsBytes = 2 * (kLdsW + kLdsA) * 2;
-  static_assert(BF % (16 * WAVES_F) == 0 && BT % (16 * WAVES_T) == 0, "wave tile");
+  static constexpr int kFeat = DUAL ? BF / 2 : BF;  // output features per workgroup
+  static_assert(kWF % 16 == 0 && kWT % 16 == 0, "wave tile");
+  static_assert(!DUAL || kMI % 2 == 0, "dual wave tile");
   static_assert(BK % 32 == 0, "k step");
+  // Uneven splits of the copy work need guards (small tiles only).
+  static constexpr bool kWGuard = kWBlocks % kThreads != 0;
+  static_assert(kAChunks % kThreads == 0, "token copy split");
 };
 
-template <int BF, int BT, int BK, int WAVES_F, int WAVES_T, bool DUAL>
-__global__ __launch_bounds__(64 * WAVES_F * WAVES_T) void grouped_gemm_bf16_kernel(GemmArgs args) {
-  using C = GemmCfg<BF, BT, BK, WAVES_F, WAVES_T, DUAL>;
+template <int BF, int BT, int BK, bool DUAL>
+__global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs args) {
+  using C = GemmCfg<BF, BT, BK, DUAL>;
   extern __shared__ __align__(16) bf16_t lds[];
 
-  const int tiles_f = args.N / BF;
-  const int ttile = blockIdx.x % args.max_tiles;
-  const int ftile = blockIdx.x / args.max_tiles;
+  // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a
+  // contiguous range of (feature tile, token tile) so the token tiles that
+  // share a weight tile run together and hit in that XCD's L2.
+  const int G = gridDim.x;
+  const int v = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+  const int tiles_f = args.N / C::kFeat;
+  const int ftile = v / args.max_tiles;
+  const int ttile = v % args.max_tiles;
+  if (ftile >= tiles_f) return;
   int e, row_begin, row_end;
   if (!find_tile(args.offsets, args.E, BT, ttile, e, row_begin, row_end)) return;
-  if (ftile >= tiles_f) return;
-  const int f0 = ftile * BF;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int fw = (wave % WAVES_F) * C::kWF;
-  const int tw = (wave / WAVES_F) * C::kWT;
+  const int wf = wave & 1;
+  const int wt = wave >> 1;
+  const int64_t N = args.N;
+  const int fbase = ftile * C::kFeat;  // first output feature of the tile
 
   const bf16_t* Wm[2];
   Wm[0] = static_cast<const bf16_t*>(args.Wa.p[e]);
   Wm[1] = DUAL ? static_cast<const bf16_t*>(args.Wb.p[e]) : Wm[0];
-  const int64_t N = args.N;
 
-  // Token rows this thread copies (fixed across k).
-  const bf16_t* a_src[C::kAPerThread];
-  int a_lds[C::kAPerThread];
+  // Token rows this thread copies (fixed across k); rows past the segment
+  // read the segment's last row (their outputs are never stored).
+  // (row index, not pointer, to save registers; the chunk column is the same
+  // for all of a thread's rows)
+  int a_row[C::kAPerThread];
+  const int a_kc = (tid % C::kKB) * 8;
 #pragma unroll
   for (int i = 0; i < C::kAPerThread; ++i) {
     const int q = tid + i * C::kThreads;
-    const int row = q / C::kKB;
-    const int kc = q % C::kKB;
-    const int r = row_begin + row;
-    a_src[i] = nullptr;
-    a_lds[i] = -1;
-    if (q < C::kAChunks) {
-      a_lds[i] = row * C::kStride + kc * 8;
-      if (r < row_end) {
-        const int64_t src_row = args.gather ? args.gather[r] : r;
-        a_src[i] = args.A + src_row * args.Kdim + kc * 8;
-      }
-    }
+    const int r = min(row_begin + q / C::kKB, row_end - 1);
+    a_row[i] = args.gather ? args.gather[r] : r;
+  }
+  const bf16_t* a_base = args.A + a_kc;
+  // Weight 8x8 blocks this thread copies: k-block fastest so that eight
+  // consecutive lanes fill one 128-byte LDS row segment.
+  const bf16_t* w_src[C::kWPerThread];
+  int w_lds[C::kWPerThread];
+#pragma unroll
+  for (int i = 0; i < C::kWPerThread; ++i) {
+    const int q = min(tid + i * C::kThreads, C::kWBlocks - 1);
+    const int kb = q % C::kKB;
+    const int fb = q / C::kKB;  // 8-column block inside the tile
+    const int mat = DUAL ? fb / (BF / 16) : 0;
+    const int col = DUAL ? (fb % (BF / 16)) * 8 : fb * 8;
+    w_lds[i] = fb * 8 * C::kStride + kb * 8;
+    w_src[i] = Wm[mat] + (int64_t)(kb * 8) * N + fbase + col;
   }
 
-  uint4 wreg[C::kWPerThread][8];
-  uint4 areg[C::kAPerThread];
+  u32x4_t wreg[C::kWPerThread][8];
+  u32x4_t areg[C::kAPerThread];
 
   auto load_tiles = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < C::kWPerThread; ++i) {
-      const int q = tid + i * C::kThreads;
-      if (q < C::kWBlocks) {
-        const int mat = q / (C::kKB * (BF / 8));
-        const int rem = q % (C::kKB * (BF / 8));
-        const int kb = rem % C::kKB;
-        const int fb = rem / C::kKB;
-        const bf16_t* src = Wm[mat] + (int64_t)(k0 + kb * 8) * N + f0 + fb * 8;
+      if (C::kWGuard && tid + i * C::kThreads >= C::kWBlocks) continue;
+      const bf16_t* src = w_src[i] + (int64_t)k0 * N;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) wreg[i][r] = *reinterpret_cast<const uint4*>(src + r * N);
-      }
+      for (int r = 0; r < 8; ++r) wreg[i][r] = *reinterpret_cast<const u32x4_t*>(src + r * N);
     }
 #pragma unroll
-    for (int i = 0; i < C::kAPerThread; ++i) {
-      if (a_src[i])
-        areg[i] = *reinterpret_cast<const uint4*>(a_src[i] + k0);
-      else
-        areg[i] = make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < C::kAPerThread; ++i)
+      areg[i] = *reinterpret_cast<const u32x4_t*>(a_base + (int64_t)a_row[i] * args.Kdim + k0);
   };
 
   auto store_tiles = [&](int buf) {
@@ -168,31 +174,33 @@ __global__ __launch_bounds__(64 * WAVES_F * WAVES_T) void grouped_gemm_bf16_kern
     bf16_t* sA = sW + C::kLdsW;
 #pragma unroll
     for (int i = 0; i < C::kWPerThread; ++i) {
-      const int q = tid + i * C::kThreads;
-      if (q < C::kWBlocks) {
-        const int mat = q / (C::kKB * (BF / 8));
-        const int rem = q % (C::kKB * (BF / 8));
-        const int kb = rem % C::kKB;
-        const int fb = rem / C::kKB;
-        uint4 cols[8];
-        transpose8x8(wreg[i], cols);
-        bf16_t* dst = sW + (mat * BF + fb * 8) * C::kStride + kb * 8;
+      if (C::kWGuard && tid + i * C::kThreads >= C::kWBlocks) continue;
+      u32x4_t cols[8];
+      transpose8x8(wreg[i], cols);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(dst + c * C::kStride) = cols[c];
-      }
+      for (int c = 0; c < 8; ++c)
+        *reinterpret_cast<u32x4_t*>(sW + w_lds[i] + c * C::kStride) = cols[c];
     }
 #pragma unroll
     for (int i = 0; i < C::kAPerThread; ++i)
-      if (a_lds[i] >= 0) *reinterpret_cast<uint4*>(sA + a_lds[i]) = areg[i];
+      *reinterpret_cast<u32x4_t*>(sA + ((tid + i * C::kThreads) / C::kKB) * C::kStride + a_kc) =
+          areg[i];
   };
 
-  f32x4_t acc[C::kMats][C::kMI][C::kNJ];
+  // LDS row of the wave's i-th 16-row group of weight columns.
+  auto wrow = [&](int i) {
+    if (DUAL) {
+      constexpr int half = C::kMI / 2;
+      return i < half ? wf * (C::kWF / 2) + 16 * i : BF / 2 + wf * (C::kWF / 2) + 16 * (i - half);
+    }
+    return wf * C::kWF + 16 * i;
+  };
+
+  f32x4_t acc[C::kMI][C::kNJ];
 #pragma unroll
-  for (int m = 0; m < C::kMats; ++m)
+  for (int i = 0; i < C::kMI; ++i)
 #pragma unroll
-    for (int i = 0; i < C::kMI; ++i)
-#pragma unroll
-      for (int j = 0; j < C::kNJ; ++j) acc[m][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < C::kNJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nk = args.Kdim / BK;
   load_tiles(0);
@@ -211,17 +219,15 @@ __global__ __launch_bounds__(64 * WAVES_F * WAVES_T) void grouped_gemm_bf16_kern
       bf16x8_t b[C::kNJ];
 #pragma unroll
       for (int j = 0; j < C::kNJ; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(sA + (tw + j * 16 + lrow) * C::kStride + ks + lk);
+        b[j] = *reinterpret_cast<const bf16x8_t*>(sA + (wt * C::kWT + j * 16 + lrow) * C::kStride +
+                                                  ks + lk);
 #pragma unroll
-      for (int m = 0; m < C::kMats; ++m) {
+      for (int i = 0; i < C::kMI; ++i) {
+        const bf16x8_t a =
+            *reinterpret_cast<const bf16x8_t*>(sW + (wrow(i) + lrow) * C::kStride + ks + lk);
 #pragma unroll
-        for (int i = 0; i < C::kMI; ++i) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-              sW + (m * BF + fw + i * 16 + lrow) * C::kStride + ks + lk);
-#pragma unroll
-          for (int j = 0; j < C::kNJ; ++j)
-            acc[m][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[m][i][j], 0, 0, 0);
-        }
+        for (int j = 0; j < C::kNJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[i][j], 0, 0, 0);
       }
     }
     if (kt + 1 < nk) store_tiles(cur ^ 1);
@@ -232,20 +238,24 @@ __global__ __launch_bounds__(64 * WAVES_F * WAVES_T) void grouped_gemm_bf16_kern
   const int fq = (lane >> 4) * 4;
 #pragma unroll
   for (int j = 0; j < C::kNJ; ++j) {
-    const int r = row_begin + tw + j * 16 + lrow;
+    const int r = row_begin + wt * C::kWT + j * 16 + lrow;
     if (r >= row_end) continue;
+    if constexpr (DUAL) {
 #pragma unroll
-    for (int i = 0; i < C::kMI; ++i) {
-      const int f = f0 + fw + i * 16 + fq;
-      if constexpr (DUAL) {
-        const f32x4_t a = acc[0][i][j];
-        const f32x4_t bb = acc[1][i][j];
-        uint2 v;
-        v.x = pack_bf16x2(silu_f32(a[0]) * bb[0], silu_f32(a[1]) * bb[1]);
-        v.y = pack_bf16x2(silu_f32(a[2]) * bb[2], silu_f32(a[3]) * bb[3]);
-        *reinterpret_cast<uint2*>(static_cast<bf16_t*>(args.out) + (int64_t)r * N + f) = v;
-      } else {
-        const f32x4_t a = acc[0][i][j];
+      for (int i = 0; i < C::kMI / 2; ++i) {
+        const int f = fbase + wf * (C::kWF / 2) + i * 16 + fq;
+        const f32x4_t a = acc[i][j];
+        const f32x4_t bb = acc[i + C::kMI / 2][j];
+        uint2 v2;
+        v2.x = pack_bf16x2(silu_f32(a[0]) * bb[0], silu_f32(a[1]) * bb[1]);
+        v2.y = pack_bf16x2(silu_f32(a[2]) * bb[2], silu_f32(a[3]) * bb[3]);
+        *reinterpret_cast<uint2*>(static_cast<bf16_t*>(args.out) + (int64_t)r * N + f) = v2;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::kMI; ++i) {
+        const int f = fbase + wf * C::kWF + i * 16 + fq;
+        const f32x4_t a = acc[i][j];
         *reinterpret_cast<float4*>(static_cast<float*>(args.out) + (int64_t)r * N + f) =
             make_float4(a[0], a[1], a[2], a[3]);
       }
@@ -253,19 +263,20 @@ __global__ __launch_bounds__(64 * WAVES_F * WAVES_T) void grouped_gemm_bf16_kern
   }
 }
 
-template <int BF, int BT, int BK, int WAVES_F, int WAVES_T, bool DUAL>
+template <int BF, int BT, int BK, bool DUAL>
 hipError_t launch_cfg(const GemmArgs& args_in, int P, int E, hipStream_t stream) {
-  using C = GemmCfg<BF, BT, BK, WAVES_F, WAVES_T, DUAL>;
+  using C = GemmCfg<BF, BT, BK, DUAL>;
   GemmArgs args = args_in;
   // sum_e ceil(n_e / BT) <= floor((P + E * (BT - 1)) / BT)
   args.max_tiles = (int)(((int64_t)P + (int64_t)E * (BT - 1)) / BT);
   if (args.max_tiles <= 0) return hipSuccess;
-  const int tiles_f = args.N / BF;
-  auto kern = grouped_gemm_bf16_kernel<BF, BT, BK, WAVES_F, WAVES_T, DUAL>;
+  const int tiles_f = args.N / C::kFeat;
+  auto kern = grouped_gemm_bf16_kernel<BF, BT, BK, DUAL>;
   hipError_t err = allow_dynamic_lds(reinterpret_cast<const void*>(kern), C::kLdsBytes);
   if (err != hipSuccess) return err;
-  dim3 grid((unsigned)args.max_tiles * (unsigned)tiles_f);
-  hipLaunchKernelGGL(kern, grid, dim3(C::kThreads), C::kLdsBytes, stream, args);
+  int64_t blocks = (int64_t)args.max_tiles * tiles_f;
+  blocks = (blocks + 7) / 8 * 8;  // whole XCD rounds for the remapped order
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(C::kThreads), C::kLdsBytes, stream, args);
   return hipGetLastError();
 }
 
@@ -285,8 +296,8 @@ hipError_t launch_expert_swiglu_bf16(const void* x, const int32_t* sorted_token,
   a.Kdim = d;
   a.N = d_ff;
   a.E = E;
-  if (P <= 64) return launch_cfg<128, 16, 64, 4, 1, true>(a, P, E, stream);
-  return launch_cfg<128, 128, 64, 2, 2, true>(a, P, E, stream);
+  if (d_ff % 128 == 0 && P > 0) return launch_cfg<256, 256, 64, true>(a, P, E, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_expert_down_bf16(const void* H, const ExpertPtrs& W2, const int32_t* offsets,
@@ -301,12 +312,8 @@ hipError_t launch_expert_down_bf16(const void* H, const ExpertPtrs& W2, const in
   a.Kdim = d_ff;
   a.N = d;
   a.E = E;
-  if (d % 256 == 0) {
-    if (P <= 64) return launch_cfg<256, 16, 64, 4, 1, false>(a, P, E, stream);
-    return launch_cfg<256, 128, 64, 2, 2, false>(a, P, E, stream);
-  }
-  if (P <= 64) return launch_cfg<128, 16, 64, 4, 1, false>(a, P, E, stream);
-  return launch_cfg<128, 128, 64, 2, 2, false>(a, P, E, stream);
+  if (d % 256 == 0) return launch_cfg<256, 256, 64, false>(a, P, E, stream);
+  return launch_cfg<128, 256, 64, false>(a, P, E, stream);
 }
 
 }  // namespace moe

@@ -1,0 +1,317 @@
+// Grouped bf16 matrix-core GEMMs for large batches (prefill), CDNA4 form.
+//
+// Same products as the other expert kernels ("从Mistral 7B到MoE模型Mixtral
+// 8x7B的全面解析" (aiqianji.com) section 3.2.4, code block D): rows arrive
+// expert-sorted, a workgroup owns one (token tile, feature tile) of one
+// expert and finds it from the offsets on the device.
+//
+// Data path (gfx950):
+//   * both operand tiles travel global -> LDS with global_load_lds_dwordx4
+//     (each instruction lands 64 lanes x 16 bytes contiguously), no register
+//     staging; a four-slot LDS ring keeps three k-stages in flight;
+//   * the weight tile stays in its [k][feature] layout in LDS and the
+//     matrix-core operand (8 consecutive k of one feature per lane) is read
+//     with ds_read_b64_tr_b16: in each 16-lane group, lane i addresses 4
+//     features of k-row (i / 4), and lane j receives element j % 4 of lanes
+//     j / 4 + 4q, i.e. 4 consecutive k of one feature;
+//   * 16-byte chunks are XOR-swizzled per row so the transposed reads and
+//     the token-operand reads are free of LDS bank conflicts;
+//   * each slot is its own __shared__ object and the k loop is unrolled over
+//     the four slots, so the compiler can prove a slot's reads independent of
+//     the loads in flight to the other slots; waits are explicit vmcnt counts
+//     followed by a bare s_barrier;
+//   * 256 weight columns x 256 tokens per workgroup (with W1/W3: 128 H
+//     features of each), four waves of 128 x 128, v_mfma_f32_16x16x32_bf16,
+//     fp32 accumulators in AGPRs; D is [feature][token], so the epilogue
+//     writes 4 consecutive features per lane (SiLU(a) * b fused for W1/W3);
+//   * tiles are ordered so that one XCD runs the token tiles sharing a
+//     weight tile together (L2 reuse).
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void global_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+constexpr int kBF = 256;       // weight columns per workgroup
+constexpr int kBK = 32;        // k per stage
+constexpr int kSlots = 4;      // LDS ring depth
+constexpr int kRowBytesW = kBF * 2;   // 512
+constexpr int kRowBytesA = kBK * 2;   // 64
+
+struct TiledArgs {
+  const bf16_t* A;         // [rows, Kdim] activations
+  const int32_t* gather;   // sorted_token, or null when A is already sorted
+  const int32_t* offsets;  // [E + 1]
+  ExpertPtrs Wa;
+  ExpertPtrs Wb;
+  void* out;               // H bf16 [P, N] (dual) or O fp32 [P, N]
+  int Kdim;
+  int N;                   // output features (d_ff, or d)
+  int E;
+  int max_tiles;
+};
+
+// Chunk swizzles (16-byte chunks): weight rows hold 32 chunks, token rows 4.
+__device__ __forceinline__ int swz_w(int r) { return 2 * (r & 3) + 8 * ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_a(int t) { return (t >> 2) & 3; }
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds((global_void_t*)src, (lds_void_t*)lds_dst, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) only (expcnt and lgkmcnt left at their maxima).
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BT, bool DUAL>
+struct TiledCfg {
+  static constexpr int kWT = BT / 2;           // tokens per wave
+  static constexpr int kNJ = kWT / 16;
+  static constexpr int kMI = 8;                // 128 weight columns per wave
+  static constexpr int kSlotW = kBK * kRowBytesW;  // 16 KB
+  static constexpr int kSlotA = BT * kRowBytesA;   // 16 KB at BT = 256
+  static constexpr int kWInstr = kSlotW / 1024 / 4;  // per wave per stage
+  static constexpr int kAInstr = kSlotA / 1024 / 4;
+  static constexpr int kDmaPerStage = kWInstr + kAInstr;
+  static constexpr int kFeat = DUAL ? kBF / 2 : kBF;
+  static_assert(kSlotA % 4096 == 0, "token tile copy split");
+};
+
+template <int BT, bool DUAL>
+__global__ __launch_bounds__(256) void tiled_gemm_kernel(TiledArgs args) {
+  using C = TiledCfg<BT, DUAL>;
+  __shared__ __align__(1024) char sW0[C::kSlotW], sW1[C::kSlotW], sW2[C::kSlotW], sW3[C::kSlotW];
+  __shared__ __align__(1024) char sA0[C::kSlotA], sA1[C::kSlotA], sA2[C::kSlotA], sA3[C::kSlotA];
+
+  const int G = gridDim.x;
+  const int v = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+  const int tiles_f = args.N / C::kFeat;
+  const int ftile = v / args.max_tiles;
+  const int ttile = v % args.max_tiles;
+  if (ftile >= tiles_f) return;
+  int e, row_begin, row_end;
+  if (!find_tile(args.offsets, args.E, BT, ttile, e, row_begin, row_end)) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wf = wave & 1;
+  const int wt = wave >> 1;
+  const int64_t N = args.N;
+  const int fbase = ftile * C::kFeat;
+
+  // ---- copy assignment (fixed across k) ----
+  // weight instruction u of this wave fills LDS rows 2*ii, 2*ii+1 (ii = wave*kWInstr + u)
+  const char* wsrc[C::kWInstr];
+#pragma unroll
+  for (int u = 0; u < C::kWInstr; ++u) {
+    const int ii = wave * C::kWInstr + u;
+    const int r = 2 * ii + (lane >> 5);
+    const int c = (lane & 31) ^ swz_w(r);     // chunk of weight columns [8c, 8c + 8)
+    const bf16_t* base;
+    int col;
+    if (DUAL) {
+      base = static_cast<const bf16_t*>(c < 16 ? args.Wa.p[e] : args.Wb.p[e]);
+      col = 8 * (c & 15);
+    } else {
+      base = static_cast<const bf16_t*>(args.Wa.p[e]);
+      col = 8 * c;
+    }
+    wsrc[u] = reinterpret_cast<const char*>(base + (int64_t)r * N + fbase + col);
+  }
+  // token instruction u fills token rows 16*jj .. 16*jj+15 (jj = wave*kAInstr + u)
+  const char* asrc[C::kAInstr];
+#pragma unroll
+  for (int u = 0; u < C::kAInstr; ++u) {
+    const int jj = wave * C::kAInstr + u;
+    const int t = 16 * jj + (lane >> 2);
+    const int c = (lane & 3) ^ swz_a(t);
+    const int r = min(row_begin + t, row_end - 1);   // rows past the segment: never stored
+    const int64_t src_row = args.gather ? args.gather[r] : r;
+    asrc[u] = reinterpret_cast<const char*>(args.A + src_row * args.Kdim + 8 * c);
+  }
+  const int64_t wstep = (int64_t)kBK * N * 2;   // bytes per stage along k
+  const int astep = kBK * 2;
+
+  char* const sW[kSlots] = {sW0, sW1, sW2, sW3};
+  char* const sA[kSlots] = {sA0, sA1, sA2, sA3};
+
+  auto issue = [&](int stage, char* w_dst, char* a_dst) {
+#pragma unroll
+    for (int u = 0; u < C::kWInstr; ++u)
+      dma16(wsrc[u] + stage * wstep, w_dst + (wave * C::kWInstr + u) * 1024);
+#pragma unroll
+    for (int u = 0; u < C::kAInstr; ++u)
+      dma16(asrc[u] + stage * astep, a_dst + (wave * C::kAInstr + u) * 1024);
+  };
+
+  // ---- operand read offsets (bytes inside a slot) ----
+  const int g = lane >> 4;
+  const int j = lane & 15;
+  // weight column group i of this wave: 16 columns starting at LDS column n0(i)
+  int a_off[C::kMI][2];
+#pragma unroll
+  for (int i = 0; i < C::kMI; ++i) {
+    int n0;
+    if (DUAL)
+      n0 = (i < 4) ? wf * 64 + 16 * i : 128 + wf * 64 + 16 * (i - 4);
+    else
+      n0 = wf * 128 + 16 * i;
+    const int n = n0 + 4 * (j & 3);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * g + 4 * h + (j >> 2);
+      a_off[i][h] = r * kRowBytesW + (((n >> 3) ^ swz_w(r)) << 4) + (n & 7) * 2;
+    }
+  }
+  int b_off[C::kNJ];
+#pragma unroll
+  for (int jb = 0; jb < C::kNJ; ++jb) {
+    const int t = wt * C::kWT + 16 * jb + j;
+    b_off[jb] = t * kRowBytesA + ((g ^ swz_a(t)) << 4);
+  }
+
+  f32x4_t acc[C::kMI][C::kNJ];
+#pragma unroll
+  for (int i = 0; i < C::kMI; ++i)
+#pragma unroll
+    for (int jb = 0; jb < C::kNJ; ++jb) acc[i][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  bf16x8_t fa[C::kMI], fb[C::kNJ];
+  auto read_frags = [&](const char* w_src, const char* a_src) {
+#pragma unroll
+    for (int jb = 0; jb < C::kNJ; ++jb)
+      fb[jb] = *reinterpret_cast<const bf16x8_t*>(a_src + b_off[jb]);
+#pragma unroll
+    for (int i = 0; i < C::kMI; ++i) {
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)((lds_char_t*)w_src + a_off[i][0]));
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)((lds_char_t*)w_src + a_off[i][1]));
+      const s16x4_t both[2] = {lo, hi};
+      fa[i] = __builtin_bit_cast(bf16x8_t, both);
+    }
+  };
+  auto mma = [&]() {
+#pragma unroll
+    for (int i = 0; i < C::kMI; ++i)
+#pragma unroll
+      for (int jb = 0; jb < C::kNJ; ++jb)
+        acc[i][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[jb], acc[i][jb], 0, 0, 0);
+  };
+
+  // nk is a multiple of kSlots (Kdim % 128 == 0).  Every stage issues the
+  // same number of loads -- past the end it reloads the last k-stage into the
+  // free slot -- so a constant vmcnt marks "this stage has landed" on every
+  // path, which keeps the compiler's own wait analysis exact.
+  const int nk = args.Kdim / kBK;
+#pragma unroll
+  for (int s = 0; s < kSlots - 1; ++s) issue(s, sW[s], sA[s]);
+
+  for (int k0 = 0; k0 < nk; k0 += kSlots) {
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+      const int kt = k0 + s;
+      wait_vm<2 * C::kDmaPerStage>();   // stages kt+1, kt+2 may still be in flight
+      __builtin_amdgcn_s_barrier();
+      // read this slot's operands, then refill the slot every wave finished
+      // reading in the previous stage, then multiply
+      read_frags(sW[s], sA[s]);
+      issue(min(kt + kSlots - 1, nk - 1), sW[(s + kSlots - 1) % kSlots],
+            sA[(s + kSlots - 1) % kSlots]);
+      mma();
+    }
+  }
+  wait_vm<0>();  // no load may land in LDS after the workgroup ends
+
+  // ---- epilogue: lane holds features f .. f+3 of token column j ----
+  const int fq = g * 4;
+#pragma unroll
+  for (int jb = 0; jb < C::kNJ; ++jb) {
+    const int r = row_begin + wt * C::kWT + jb * 16 + j;
+    if (r >= row_end) continue;
+    if constexpr (DUAL) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int f = fbase + wf * 64 + i * 16 + fq;
+        const f32x4_t a = acc[i][jb];
+        const f32x4_t bb = acc[i + 4][jb];
+        uint2 v2;
+        v2.x = pack_bf16x2(silu_f32(a[0]) * bb[0], silu_f32(a[1]) * bb[1]);
+        v2.y = pack_bf16x2(silu_f32(a[2]) * bb[2], silu_f32(a[3]) * bb[3]);
+        *reinterpret_cast<uint2*>(static_cast<bf16_t*>(args.out) + (int64_t)r * N + f) = v2;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::kMI; ++i) {
+        const int f = fbase + wf * 128 + i * 16 + fq;
+        const f32x4_t a = acc[i][jb];
+        *reinterpret_cast<float4*>(static_cast<float*>(args.out) + (int64_t)r * N + f) =
+            make_float4(a[0], a[1], a[2], a[3]);
+      }
+    }
+  }
+}
+
+template <int BT, bool DUAL>
+hipError_t launch_tiled(const TiledArgs& in, int P, hipStream_t stream) {
+  using C = TiledCfg<BT, DUAL>;
+  TiledArgs a = in;
+  a.max_tiles = (int)(((int64_t)P + (int64_t)a.E * (BT - 1)) / BT);
+  if (a.max_tiles <= 0) return hipSuccess;
+  int64_t blocks = (int64_t)a.max_tiles * (a.N / C::kFeat);
+  blocks = (blocks + 7) / 8 * 8;  // whole XCD rounds for the remapped order
+  hipLaunchKernelGGL((tiled_gemm_kernel<BT, DUAL>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                     a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool tiled_gemm_supported(int Kdim, int N, bool dual) {
+  return Kdim % (kBK * kSlots) == 0 && N % (dual ? kBF / 2 : kBF) == 0;
+}
+
+hipError_t launch_tiled_swiglu_bf16(const void* x, const int32_t* sorted_token,
+                                    const ExpertPtrs& W1, const ExpertPtrs& W3,
+                                    const int32_t* offsets, int P, int d, int d_ff, int E,
+                                    void* H, hipStream_t stream) {
+  TiledArgs a{};
+  a.A = static_cast<const bf16_t*>(x);
+  a.gather = sorted_token;
+  a.offsets = offsets;
+  a.Wa = W1;
+  a.Wb = W3;
+  a.out = H;
+  a.Kdim = d;
+  a.N = d_ff;
+  a.E = E;
+  return launch_tiled<256, true>(a, P, stream);
+}
+
+hipError_t launch_tiled_down_bf16(const void* H, const ExpertPtrs& W2, const int32_t* offsets,
+                                  int P, int d, int d_ff, int E, float* O, hipStream_t stream) {
+  TiledArgs a{};
+  a.A = static_cast<const bf16_t*>(H);
+  a.gather = nullptr;
+  a.offsets = offsets;
+  a.Wa = W2;
+  a.Wb = W2;
+  a.out = O;
+  a.Kdim = d_ff;
+  a.N = d;
+  a.E = E;
+  return launch_tiled<256, false>(a, P, stream);
+}
+
+}  // namespace moe

@@ -253,6 +253,8 @@ hipError_t run_swiglu(const Plan& plan, const void* x, const int32_t* sorted_tok
   if (plan.streaming)
     return moe::launch_stream_swiglu_bf16(x, sorted_token, p1, p3, offsets, P, d, d_ff, E,
                                           plan.swiglu_splits, static_cast<float*>(scratch), H, st);
+  if (moe::tiled_gemm_supported(d, d_ff, true))
+    return moe::launch_tiled_swiglu_bf16(x, sorted_token, p1, p3, offsets, P, d, d_ff, E, H, st);
   return moe::launch_expert_swiglu_bf16(x, sorted_token, p1, p3, offsets, P, d, d_ff, E, H, st);
 }
 
@@ -262,6 +264,8 @@ hipError_t run_down(const Plan& plan, const void* H, const moe::ExpertPtrs& p2,
   if (dtype != MOE_BF16) return moe::launch_expert_down_f32(H, p2, offsets, P, d, d_ff, E, O, st);
   if (plan.streaming)
     return moe::launch_stream_down_bf16(H, p2, offsets, P, d, d_ff, E, plan.down_splits, O, st);
+  if (moe::tiled_gemm_supported(d_ff, d, false))
+    return moe::launch_tiled_down_bf16(H, p2, offsets, P, d, d_ff, E, O, st);
   return moe::launch_expert_down_bf16(H, p2, offsets, P, d, d_ff, E, O, st);
 }
 
