@@ -39,6 +39,9 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void global_void_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
 
+#ifndef MOE_TILED_WT
+#define MOE_TILED_WT 4
+#endif
 constexpr int kBF = 256;       // weight columns per workgroup
 constexpr int kBK = 32;        // k per stage
 constexpr int kSlots = 4;      // LDS ring depth
@@ -51,11 +54,13 @@ struct TiledArgs {
   const int32_t* offsets;  // [E + 1]
   ExpertPtrs Wa;
   ExpertPtrs Wb;
-  void* out;               // H bf16 [P, N] (dual) or O fp32 [P, N]
+  void* out;               // H bf16 [P, N] (dual) or O fp32 [splits, P, N]
   int Kdim;
   int N;                   // output features (d_ff, or d)
   int E;
+  int P;
   int max_tiles;
+  int splits;              // K splits (one output slice each; 1 for W1/W3)
 };
 
 // Chunk swizzles (16-byte chunks): weight rows hold 32 chunks, token rows 4.
@@ -73,32 +78,35 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int BT, bool DUAL>
+template <int BT, int WT, bool DUAL>
 struct TiledCfg {
-  static constexpr int kWT = BT / 2;           // tokens per wave
+  static constexpr int kWaves = 2 * WT;        // 2 along weight columns x WT along tokens
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kWT = BT / WT;          // tokens per wave
   static constexpr int kNJ = kWT / 16;
   static constexpr int kMI = 8;                // 128 weight columns per wave
   static constexpr int kSlotW = kBK * kRowBytesW;  // 16 KB
   static constexpr int kSlotA = BT * kRowBytesA;   // 16 KB at BT = 256
-  static constexpr int kWInstr = kSlotW / 1024 / 4;  // per wave per stage
-  static constexpr int kAInstr = kSlotA / 1024 / 4;
+  static constexpr int kWInstr = kSlotW / 1024 / kWaves;  // per wave per stage
+  static constexpr int kAInstr = kSlotA / 1024 / kWaves;
   static constexpr int kDmaPerStage = kWInstr + kAInstr;
   static constexpr int kFeat = DUAL ? kBF / 2 : kBF;
-  static_assert(kSlotA % 4096 == 0, "token tile copy split");
+  static_assert(kSlotA % (1024 * kWaves) == 0 && kSlotW % (1024 * kWaves) == 0, "copy split");
 };
 
-template <int BT, bool DUAL>
-__global__ __launch_bounds__(256) void tiled_gemm_kernel(TiledArgs args) {
-  using C = TiledCfg<BT, DUAL>;
+template <int BT, int WT, bool DUAL>
+__global__ __launch_bounds__(128 * WT) void tiled_gemm_kernel(TiledArgs args) {
+  using C = TiledCfg<BT, WT, DUAL>;
   __shared__ __align__(1024) char sW0[C::kSlotW], sW1[C::kSlotW], sW2[C::kSlotW], sW3[C::kSlotW];
   __shared__ __align__(1024) char sA0[C::kSlotA], sA1[C::kSlotA], sA2[C::kSlotA], sA3[C::kSlotA];
 
   const int G = gridDim.x;
   const int v = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
   const int tiles_f = args.N / C::kFeat;
-  const int ftile = v / args.max_tiles;
   const int ttile = v % args.max_tiles;
-  if (ftile >= tiles_f) return;
+  const int ftile = (v / args.max_tiles) % tiles_f;
+  const int split = v / args.max_tiles / tiles_f;
+  if (split >= args.splits) return;
   int e, row_begin, row_end;
   if (!find_tile(args.offsets, args.E, BT, ttile, e, row_begin, row_end)) return;
 
@@ -109,6 +117,7 @@ __global__ __launch_bounds__(256) void tiled_gemm_kernel(TiledArgs args) {
   const int wt = wave >> 1;
   const int64_t N = args.N;
   const int fbase = ftile * C::kFeat;
+  (void)tid;
 
   // ---- copy assignment (fixed across k) ----
   // weight instruction u of this wave fills LDS rows 2*ii, 2*ii+1 (ii = wave*kWInstr + u)
@@ -142,6 +151,11 @@ __global__ __launch_bounds__(256) void tiled_gemm_kernel(TiledArgs args) {
   }
   const int64_t wstep = (int64_t)kBK * N * 2;   // bytes per stage along k
   const int astep = kBK * 2;
+  const int ksplit = args.Kdim / args.splits;    // this split's k-range
+#pragma unroll
+  for (int u = 0; u < C::kWInstr; ++u) wsrc[u] += (int64_t)split * ksplit * N * 2;
+#pragma unroll
+  for (int u = 0; u < C::kAInstr; ++u) asrc[u] += (int64_t)split * ksplit * 2;
 
   char* const sW[kSlots] = {sW0, sW1, sW2, sW3};
   char* const sA[kSlots] = {sA0, sA1, sA2, sA3};
@@ -214,7 +228,7 @@ __global__ __launch_bounds__(256) void tiled_gemm_kernel(TiledArgs args) {
   // same number of loads -- past the end it reloads the last k-stage into the
   // free slot -- so a constant vmcnt marks "this stage has landed" on every
   // path, which keeps the compiler's own wait analysis exact.
-  const int nk = args.Kdim / kBK;
+  const int nk = ksplit / kBK;
 #pragma unroll
   for (int s = 0; s < kSlots - 1; ++s) issue(s, sW[s], sA[s]);
 
@@ -256,30 +270,35 @@ __global__ __launch_bounds__(256) void tiled_gemm_kernel(TiledArgs args) {
       for (int i = 0; i < C::kMI; ++i) {
         const int f = fbase + wf * 128 + i * 16 + fq;
         const f32x4_t a = acc[i][jb];
-        *reinterpret_cast<float4*>(static_cast<float*>(args.out) + (int64_t)r * N + f) =
-            make_float4(a[0], a[1], a[2], a[3]);
+        float* o = static_cast<float*>(args.out) + ((int64_t)split * args.P + r) * N + f;
+        *reinterpret_cast<float4*>(o) = make_float4(a[0], a[1], a[2], a[3]);
       }
     }
   }
 }
 
-template <int BT, bool DUAL>
+template <int BT, int WT, bool DUAL>
 hipError_t launch_tiled(const TiledArgs& in, int P, hipStream_t stream) {
-  using C = TiledCfg<BT, DUAL>;
+  using C = TiledCfg<BT, WT, DUAL>;
   TiledArgs a = in;
   a.max_tiles = (int)(((int64_t)P + (int64_t)a.E * (BT - 1)) / BT);
   if (a.max_tiles <= 0) return hipSuccess;
-  int64_t blocks = (int64_t)a.max_tiles * (a.N / C::kFeat);
+  int64_t blocks = (int64_t)a.max_tiles * (a.N / C::kFeat) * a.splits;
   blocks = (blocks + 7) / 8 * 8;  // whole XCD rounds for the remapped order
-  hipLaunchKernelGGL((tiled_gemm_kernel<BT, DUAL>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                     a);
+  hipLaunchKernelGGL((tiled_gemm_kernel<BT, WT, DUAL>), dim3((unsigned)blocks), dim3(C::kThreads),
+                     0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool tiled_gemm_supported(int Kdim, int N, bool dual) {
-  return Kdim % (kBK * kSlots) == 0 && N % (dual ? kBF / 2 : kBF) == 0;
+bool tiled_gemm_supported(int Kdim, int N, bool dual, int splits) {
+  return splits >= 1 && Kdim % (kBK * kSlots * splits) == 0 && N % (dual ? kBF / 2 : kBF) == 0;
+}
+
+int tiled_gemm_tiles(int P, int E, int N, bool dual) {
+  const int64_t mt = ((int64_t)P + (int64_t)E * 255) / 256;
+  return (int)(mt * (N / (dual ? kBF / 2 : kBF)));
 }
 
 hipError_t launch_tiled_swiglu_bf16(const void* x, const int32_t* sorted_token,
@@ -296,11 +315,14 @@ hipError_t launch_tiled_swiglu_bf16(const void* x, const int32_t* sorted_token,
   a.Kdim = d;
   a.N = d_ff;
   a.E = E;
-  return launch_tiled<256, true>(a, P, stream);
+  a.P = P;
+  a.splits = 1;
+  return launch_tiled<256, MOE_TILED_WT, true>(a, P, stream);
 }
 
 hipError_t launch_tiled_down_bf16(const void* H, const ExpertPtrs& W2, const int32_t* offsets,
-                                  int P, int d, int d_ff, int E, float* O, hipStream_t stream) {
+                                  int P, int d, int d_ff, int E, int splits, float* O,
+                                  hipStream_t stream) {
   TiledArgs a{};
   a.A = static_cast<const bf16_t*>(H);
   a.gather = nullptr;
@@ -311,7 +333,9 @@ hipError_t launch_tiled_down_bf16(const void* H, const ExpertPtrs& W2, const int
   a.Kdim = d_ff;
   a.N = d;
   a.E = E;
-  return launch_tiled<256, false>(a, P, stream);
+  a.P = P;
+  a.splits = splits;
+  return launch_tiled<256, MOE_TILED_WT, false>(a, P, stream);
 }
 
 }  // namespace moe

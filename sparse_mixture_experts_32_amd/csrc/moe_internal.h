@@ -49,13 +49,15 @@ hipError_t launch_stream_down_bf16(const void* H, const ExpertPtrs& W2, const in
 
 // CDNA4 tiled variants for large batches (direct-to-LDS loads, transposed
 // LDS reads); need Kdim % 128 == 0 and N % 128 (W1/W3) or N % 256 (W2).
-bool tiled_gemm_supported(int Kdim, int N, bool dual);
+bool tiled_gemm_supported(int Kdim, int N, bool dual, int splits);
+int tiled_gemm_tiles(int P, int E, int N, bool dual);  // worst-case workgroups per split
 hipError_t launch_tiled_swiglu_bf16(const void* x, const int32_t* sorted_token,
                                     const ExpertPtrs& W1, const ExpertPtrs& W3,
                                     const int32_t* offsets, int P, int d, int d_ff, int E,
                                     void* H, hipStream_t stream);
 hipError_t launch_tiled_down_bf16(const void* H, const ExpertPtrs& W2, const int32_t* offsets,
-                                  int P, int d, int d_ff, int E, float* O, hipStream_t stream);
+                                  int P, int d, int d_ff, int E, int splits, float* O,
+                                  hipStream_t stream);
 
 // Lets `kernel` use `bytes` of dynamic LDS on the current device (once per
 // device and kernel).
