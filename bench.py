@@ -33,6 +33,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 HEADLINE = "decode_bf16_T8"
 SWEEP = ("mid_bf16_T512", "prefill_bf16_T4096_zipf")
+DECODE_SWEEP_T = (1, 2, 4, 16, 32, 64)
+STACK = "stack32_bf16_T4096"
 STAGES = ("router_topk", "route_permute", "expert_swiglu", "expert_down", "combine")
 
 
@@ -91,6 +93,14 @@ class Layer:
     def counts(self):
         off = self.offsets.cpu().numpy()
         return np.diff(off)
+
+    def routing_stats(self):
+        """Expert load and the share of consecutive tokens whose first-choice
+        expert repeats (uniform independent routing gives about 1/E)."""
+        idx = self.topk_idx.cpu().numpy()
+        first = idx[:, 0]
+        rep = float(np.mean(first[1:] == first[:-1])) if len(first) > 1 else None
+        return dict(first_choice_repeat_rate=None if rep is None else round(rep, 4))
 
 
 def algorithmic(w: W.Workload, counts):
@@ -194,12 +204,61 @@ def run_workload(name, dev, steps, warmup):
                ms_per_step_single_call=round(wall_fwd / steps * 1e3, 4),
                stage_ms={k: round(v, 4) for k, v in per_stage.items()},
                n_active_experts=alg["n_active"], expert_counts=counts.tolist(),
-               plan=layer.plan,
+               plan=layer.plan, routing=layer.routing_stats(),
                layer_roofline_frac=round(max(alg["layer_bytes"] / (HBM_PEAK_GBS * 1e9),
                                              alg["layer_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12))
                                          / (ms * 1e-3), 4),
                roofline=roofline_for(w, alg, per_stage))
     return res, layer
+
+
+def run_decode_sweep(dev, steps, warmup):
+    """Small batches through the decode-shape layer (T = 1 .. 64)."""
+    out = []
+    for T in DECODE_SWEEP_T:
+        w = W.scaled(W.WORKLOADS[HEADLINE], name="decode_bf16_T%d" % T, T=T)
+        layer = Layer(w, dev)
+        layer.step()
+        torch.cuda.synchronize()
+        wall, per_stage, _ = time_layer(layer, steps, warmup)
+        out.append(dict(T=T, ms_per_step=round(wall / steps * 1e3, 4),
+                        tokens_per_s=round(T * steps / wall, 1),
+                        n_active_experts=int(np.sum(layer.counts() > 0)), plan=layer.plan))
+        del layer
+        torch.cuda.empty_cache()
+    return out
+
+
+def run_stack(dev, steps, warmup):
+    """The 32-block stack (RMSNorm + MoE + residual per block, 90 GB of
+    expert weights resident), T = 4096 tokens per step."""
+    w = W.WORKLOADS[STACK]
+    blocks = [W.expert_weights(w, dev, block=b) for b in range(w.layers)]
+    h0 = W.make_x(w, blocks[0][0], dev)
+    h = h0.clone()
+    ws = torch.empty(M.workspace_size(w.T, w.d, w.d_ff, w.E, w.K, M.BF16), dtype=torch.uint8,
+                     device=dev)
+    xn = torch.empty_like(h)
+    for _ in range(warmup):
+        h.copy_(h0)
+        M.moe_stack_forward(h, blocks, w.K, workspace=ws, xn=xn)
+    torch.cuda.synchronize()
+    t = 0.0
+    for _ in range(steps):
+        h.copy_(h0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        M.moe_stack_forward(h, blocks, w.K, workspace=ws, xn=xn)
+        torch.cuda.synchronize()
+        t += time.perf_counter() - t0
+    flops = w.layers * (w.T * w.K * 6 * w.d * w.d_ff)
+    res = dict(workload=STACK, T=w.T, layers=w.layers, steps=steps,
+               ms_per_step=round(t / steps * 1e3, 3), tokens_per_s=round(w.T * steps / t, 1),
+               achieved_tflops=round(flops / (t / steps) / 1e12, 1),
+               weights_gb=round(w.layers * w.E * 3 * w.d * w.d_ff * 2 / 1e9, 1))
+    del blocks, h, h0, ws, xn
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -208,6 +267,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default=None, help="time just this workload (profiling runs)")
     args = ap.parse_args()
@@ -238,6 +298,11 @@ def main():
             sweep.append(r)
             del lay
             torch.cuda.empty_cache()
+    decode_sweep = [] if args.no_sweep else run_decode_sweep(dev, max(5, args.steps // 5), 2)
+    stack = None if (args.no_sweep or args.no_stack) else run_stack(dev, 3, 1)
+    if stack:
+        print("# %s done: %.1f ms/step" % (STACK, stack["ms_per_step"]), file=sys.stderr,
+              flush=True)
     w = W.WORKLOADS[HEADLINE]
     out = {
         "metric": "MoE-layer tokens/s at Mixtral shape (T=8/512/4096); % HBM or MFMA peak",
@@ -258,6 +323,8 @@ def main():
         "cpu_baseline": cpu,
         "detail": {k: v for k, v in head.items() if k not in ("roofline",)},
         "sweep": sweep,
+        "decode_sweep": decode_sweep,
+        "stack": stack,
     }
     print(json.dumps(out), flush=True)
 

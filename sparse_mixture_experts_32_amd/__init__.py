@@ -24,7 +24,7 @@ __all__ = [
     "MoeError", "MoeLibraryMissing", "F32", "BF16", "WS_ITEMS",
     "load_library", "plan_for", "workspace_size", "workspace_layout", "moe_forward",
     "moe_router_topk", "moe_route_permute", "moe_expert_swiglu", "moe_expert_down",
-    "moe_combine", "moe_rmsnorm", "EXPORTED_SYMBOLS",
+    "moe_combine", "moe_rmsnorm", "moe_stack_forward", "EXPORTED_SYMBOLS",
 ]
 
 F32 = 0
@@ -289,3 +289,25 @@ def moe_rmsnorm(h, out=None, eps=1e-5, stream=None):
         out = torch.empty_like(h)
     _check(lib.moe_rmsnorm(_ptr(h), _ptr(out), T, d, eps, _dtype_code(h), _stream(stream)), lib)
     return out
+
+
+def moe_stack_forward(h, blocks, K, eps=1e-5, workspace=None, xn=None, stream=None):
+    """A stack of pre-norm MoE blocks, h <- h + MoE_l(RMSNorm(h)) for every
+    block l, in place on h, through moe_rmsnorm and moe_forward(accumulate=1)
+    ("【DL輪読会】Mixtral of Experts" slides, "Architecture – 全体").
+    ``blocks`` is a sequence of (W_g, W1s, W3s, W2s).  Returns h."""
+    T, d = h.shape
+    if not blocks:
+        return h
+    E = len(blocks[0][1])
+    d_ff = blocks[0][1][0].shape[1]
+    if workspace is None:
+        workspace = torch.empty(max(workspace_size(T, d, d_ff, E, K, _dtype_code(h)), 1),
+                                dtype=torch.uint8, device=h.device)
+    if xn is None:
+        xn = torch.empty_like(h)
+    for (W_g, W1s, W3s, W2s) in blocks:
+        moe_rmsnorm(h, xn, eps=eps, stream=stream)
+        moe_forward(xn, W_g, W1s, W3s, W2s, K, y=h, accumulate=True, workspace=workspace,
+                    stream=stream)
+    return h

@@ -21,11 +21,15 @@
 //     the loads in flight to the other slots; waits are explicit vmcnt counts
 //     followed by a bare s_barrier;
 //   * 256 weight columns x 256 tokens per workgroup (with W1/W3: 128 H
-//     features of each), four waves of 128 x 128, v_mfma_f32_16x16x32_bf16,
-//     fp32 accumulators in AGPRs; D is [feature][token], so the epilogue
-//     writes 4 consecutive features per lane (SiLU(a) * b fused for W1/W3);
-//   * tiles are ordered so that one XCD runs the token tiles sharing a
-//     weight tile together (L2 reuse).
+//     features of each), eight waves of 128 x 64 (two per SIMD, so one
+//     wave's matrix instructions cover the other's LDS reads),
+//     v_mfma_f32_16x16x32_bf16 with fp32 accumulators; D is
+//     [feature][token], so the epilogue writes 4 consecutive features per
+//     lane (SiLU(a) * b fused for W1/W3); token groups of a wave that lie
+//     wholly in the padding of an expert's last tile skip their multiplies;
+//   * tile order: each XCD runs a contiguous range in which 4 feature tiles
+//     are interleaved with the token tiles, so the ~32 workgroups it runs at
+//     once share a few weight tiles and a few token tiles in its L2.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -38,13 +42,13 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void global_void_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-#ifndef MOE_TILED_WT
-#define MOE_TILED_WT 4
-#endif
 constexpr int kBF = 256;       // weight columns per workgroup
 constexpr int kBK = 32;        // k per stage
 constexpr int kSlots = 4;      // LDS ring depth
+constexpr int kWavesT = 4;     // waves along tokens (x 2 along weight columns)
+constexpr int kGroupF = 4;     // feature tiles interleaved in the tile order
 constexpr int kRowBytesW = kBF * 2;   // 512
 constexpr int kRowBytesA = kBK * 2;   // 64
 
@@ -61,6 +65,7 @@ struct TiledArgs {
   int P;
   int max_tiles;
   int splits;              // K splits (one output slice each; 1 for W1/W3)
+  int group_f;             // feature tiles interleaved in the tile order (divides N / feat)
 };
 
 // Chunk swizzles (16-byte chunks): weight rows hold 32 chunks, token rows 4.
@@ -78,11 +83,11 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int BT, int WT, bool DUAL>
+template <int BT, bool DUAL>
 struct TiledCfg {
-  static constexpr int kWaves = 2 * WT;        // 2 along weight columns x WT along tokens
+  static constexpr int kWaves = 2 * kWavesT;   // 2 along weight columns x 4 along tokens
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kWT = BT / WT;          // tokens per wave
+  static constexpr int kWT = BT / kWavesT;     // tokens per wave
   static constexpr int kNJ = kWT / 16;
   static constexpr int kMI = 8;                // 128 weight columns per wave
   static constexpr int kSlotW = kBK * kRowBytesW;  // 16 KB
@@ -94,25 +99,35 @@ struct TiledCfg {
   static_assert(kSlotA % (1024 * kWaves) == 0 && kSlotW % (1024 * kWaves) == 0, "copy split");
 };
 
-template <int BT, int WT, bool DUAL>
-__global__ __launch_bounds__(128 * WT) void tiled_gemm_kernel(TiledArgs args) {
-  using C = TiledCfg<BT, WT, DUAL>;
+template <int BT, bool DUAL>
+__global__ __launch_bounds__(128 * kWavesT) void tiled_gemm_kernel(TiledArgs args) {
+  using C = TiledCfg<BT, DUAL>;
   __shared__ __align__(1024) char sW0[C::kSlotW], sW1[C::kSlotW], sW2[C::kSlotW], sW3[C::kSlotW];
   __shared__ __align__(1024) char sA0[C::kSlotA], sA1[C::kSlotA], sA2[C::kSlotA], sA3[C::kSlotA];
+  char* const sW[kSlots] = {sW0, sW1, sW2, sW3};
+  char* const sA[kSlots] = {sA0, sA1, sA2, sA3};
 
+  // Tile order.  Workgroup b runs on XCD b % 8; each XCD gets a contiguous
+  // range of the order, in which group_f feature tiles are interleaved with
+  // the token tiles (feature fastest), so the ~32 workgroups an XCD runs at
+  // once span a few weight tiles and a few token tiles and both operands are
+  // reused from that XCD's L2.
   const int G = gridDim.x;
   const int v = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
   const int tiles_f = args.N / C::kFeat;
-  const int ttile = v % args.max_tiles;
-  const int ftile = (v / args.max_tiles) % tiles_f;
-  const int split = v / args.max_tiles / tiles_f;
+  const int per_split = args.max_tiles * tiles_f;
+  const int split = v / per_split;
   if (split >= args.splits) return;
+  const int w = v % per_split;
+  const int gf = args.group_f;
+  const int ftile = (w / (gf * args.max_tiles)) * gf + w % gf;
+  const int ttile = (w / gf) % args.max_tiles;
   int e, row_begin, row_end;
   if (!find_tile(args.offsets, args.E, BT, ttile, e, row_begin, row_end)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wf = wave & 1;
   const int wt = wave >> 1;
   const int64_t N = args.N;
@@ -120,26 +135,28 @@ __global__ __launch_bounds__(128 * WT) void tiled_gemm_kernel(TiledArgs args) {
   (void)tid;
 
   // ---- copy assignment (fixed across k) ----
-  // weight instruction u of this wave fills LDS rows 2*ii, 2*ii+1 (ii = wave*kWInstr + u)
-  const char* wsrc[C::kWInstr];
+  // The weight slot holds kSub sub-tiles (W1 and W3 for the SwiGLU product)
+  // of 32 k-rows x kSubCols features; one load instruction fills 1 KB, i.e.
+  // 1024 / kRowB consecutive rows of one sub-tile, so its source matrix is
+  // uniform and the address is a scalar base plus a 32-bit lane offset.
+  constexpr int kSub = DUAL ? 2 : 1;
+  constexpr int kSubCols = kBF / kSub;
+  constexpr int kRowB = kSubCols * 2;          // bytes per LDS row of a sub-tile
+  constexpr int kChunks = kRowB / 16;          // 16-byte chunks per row
+  constexpr int kRowsPerInstr = 1024 / kRowB;
+  uint32_t woff[C::kWInstr];
+  const char* wbase[C::kWInstr];
 #pragma unroll
   for (int u = 0; u < C::kWInstr; ++u) {
-    const int ii = wave * C::kWInstr + u;
-    const int r = 2 * ii + (lane >> 5);
-    const int c = (lane & 31) ^ swz_w(r);     // chunk of weight columns [8c, 8c + 8)
-    const bf16_t* base;
-    int col;
-    if (DUAL) {
-      base = static_cast<const bf16_t*>(c < 16 ? args.Wa.p[e] : args.Wb.p[e]);
-      col = 8 * (c & 15);
-    } else {
-      base = static_cast<const bf16_t*>(args.Wa.p[e]);
-      col = 8 * c;
-    }
-    wsrc[u] = reinterpret_cast<const char*>(base + (int64_t)r * N + fbase + col);
+    const int ii = wave * C::kWInstr + u;                 // 0 .. 15
+    const int sub = ii / (16 / kSub);
+    const int r = (ii % (16 / kSub)) * kRowsPerInstr + lane / kChunks;
+    const int c = (lane % kChunks) ^ swz_w(r);
+    wbase[u] = static_cast<const char*>(sub == 0 ? args.Wa.p[e] : args.Wb.p[e]);
+    woff[u] = (uint32_t)(((int64_t)r * N + fbase + 8 * c) * 2);
   }
   // token instruction u fills token rows 16*jj .. 16*jj+15 (jj = wave*kAInstr + u)
-  const char* asrc[C::kAInstr];
+  uint32_t aoff[C::kAInstr];
 #pragma unroll
   for (int u = 0; u < C::kAInstr; ++u) {
     const int jj = wave * C::kAInstr + u;
@@ -147,45 +164,44 @@ __global__ __launch_bounds__(128 * WT) void tiled_gemm_kernel(TiledArgs args) {
     const int c = (lane & 3) ^ swz_a(t);
     const int r = min(row_begin + t, row_end - 1);   // rows past the segment: never stored
     const int64_t src_row = args.gather ? args.gather[r] : r;
-    asrc[u] = reinterpret_cast<const char*>(args.A + src_row * args.Kdim + 8 * c);
+    aoff[u] = (uint32_t)((src_row * args.Kdim + 8 * c) * 2);
   }
   const int64_t wstep = (int64_t)kBK * N * 2;   // bytes per stage along k
   const int astep = kBK * 2;
   const int ksplit = args.Kdim / args.splits;    // this split's k-range
+  const char* abase = reinterpret_cast<const char*>(args.A) + (int64_t)split * ksplit * 2;
 #pragma unroll
-  for (int u = 0; u < C::kWInstr; ++u) wsrc[u] += (int64_t)split * ksplit * N * 2;
-#pragma unroll
-  for (int u = 0; u < C::kAInstr; ++u) asrc[u] += (int64_t)split * ksplit * 2;
-
-  char* const sW[kSlots] = {sW0, sW1, sW2, sW3};
-  char* const sA[kSlots] = {sA0, sA1, sA2, sA3};
+  for (int u = 0; u < C::kWInstr; ++u) wbase[u] += (int64_t)split * ksplit * N * 2;
 
   auto issue = [&](int stage, char* w_dst, char* a_dst) {
 #pragma unroll
     for (int u = 0; u < C::kWInstr; ++u)
-      dma16(wsrc[u] + stage * wstep, w_dst + (wave * C::kWInstr + u) * 1024);
+      dma16(wbase[u] + stage * wstep + woff[u], w_dst + (wave * C::kWInstr + u) * 1024);
 #pragma unroll
     for (int u = 0; u < C::kAInstr; ++u)
-      dma16(asrc[u] + stage * astep, a_dst + (wave * C::kAInstr + u) * 1024);
+      dma16(abase + stage * astep + aoff[u], a_dst + (wave * C::kAInstr + u) * 1024);
   };
 
   // ---- operand read offsets (bytes inside a slot) ----
   const int g = lane >> 4;
   const int j = lane & 15;
-  // weight column group i of this wave: 16 columns starting at LDS column n0(i)
+  // weight column group i of this wave: 16 columns of sub-tile sub from column n0
   int a_off[C::kMI][2];
 #pragma unroll
   for (int i = 0; i < C::kMI; ++i) {
-    int n0;
-    if (DUAL)
-      n0 = (i < 4) ? wf * 64 + 16 * i : 128 + wf * 64 + 16 * (i - 4);
-    else
+    int sub, n0;
+    if (DUAL) {
+      sub = i < 4 ? 0 : 1;
+      n0 = wf * 64 + 16 * (i & 3);
+    } else {
+      sub = 0;
       n0 = wf * 128 + 16 * i;
+    }
     const int n = n0 + 4 * (j & 3);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int r = 8 * g + 4 * h + (j >> 2);
-      a_off[i][h] = r * kRowBytesW + (((n >> 3) ^ swz_w(r)) << 4) + (n & 7) * 2;
+      a_off[i][h] = sub * (kBK * kRowB) + r * kRowB + (((n >> 3) ^ swz_w(r)) << 4) + (n & 7) * 2;
     }
   }
   int b_off[C::kNJ];
@@ -216,18 +232,23 @@ __global__ __launch_bounds__(128 * WT) void tiled_gemm_kernel(TiledArgs args) {
       fa[i] = __builtin_bit_cast(bf16x8_t, both);
     }
   };
+  // Token groups of the wave that lie wholly past the expert's segment (the
+  // padding of its last tile) are skipped: their outputs are never stored.
+  const int live_groups = min(C::kNJ, (row_end - row_begin - wt * C::kWT + 15) / 16);
   auto mma = [&]() {
 #pragma unroll
-    for (int i = 0; i < C::kMI; ++i)
+    for (int jb = 0; jb < C::kNJ; ++jb) {
+      if (jb >= live_groups) break;
 #pragma unroll
-      for (int jb = 0; jb < C::kNJ; ++jb)
+      for (int i = 0; i < C::kMI; ++i)
         acc[i][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[jb], acc[i][jb], 0, 0, 0);
+    }
   };
 
-  // nk is a multiple of kSlots (Kdim % 128 == 0).  Every stage issues the
-  // same number of loads -- past the end it reloads the last k-stage into the
-  // free slot -- so a constant vmcnt marks "this stage has landed" on every
-  // path, which keeps the compiler's own wait analysis exact.
+  // nk is a multiple of kSlots (Kdim % 128 == 0 per split).  Every stage
+  // issues the same number of loads -- past the end it reloads the last
+  // k-stage into the free slot -- so a constant vmcnt marks "this stage has
+  // landed" on every path, which keeps the compiler's own wait analysis exact.
   const int nk = ksplit / kBK;
 #pragma unroll
   for (int s = 0; s < kSlots - 1; ++s) issue(s, sW[s], sA[s]);
@@ -236,8 +257,8 @@ __global__ __launch_bounds__(128 * WT) void tiled_gemm_kernel(TiledArgs args) {
 #pragma unroll
     for (int s = 0; s < kSlots; ++s) {
       const int kt = k0 + s;
-      wait_vm<2 * C::kDmaPerStage>();   // stages kt+1, kt+2 may still be in flight
-      __builtin_amdgcn_s_barrier();
+      wait_vm<(kSlots - 2) * C::kDmaPerStage>();   // stage kt landed; later ones may not have
+      __builtin_amdgcn_s_barrier();                // ... for every wave; slot of kt-1 is free
       // read this slot's operands, then refill the slot every wave finished
       // reading in the previous stage, then multiply
       read_frags(sW[s], sA[s]);
@@ -277,16 +298,19 @@ __global__ __launch_bounds__(128 * WT) void tiled_gemm_kernel(TiledArgs args) {
   }
 }
 
-template <int BT, int WT, bool DUAL>
+template <int BT, bool DUAL>
 hipError_t launch_tiled(const TiledArgs& in, int P, hipStream_t stream) {
-  using C = TiledCfg<BT, WT, DUAL>;
+  using C = TiledCfg<BT, DUAL>;
   TiledArgs a = in;
   a.max_tiles = (int)(((int64_t)P + (int64_t)a.E * (BT - 1)) / BT);
   if (a.max_tiles <= 0) return hipSuccess;
-  int64_t blocks = (int64_t)a.max_tiles * (a.N / C::kFeat) * a.splits;
+  const int tiles_f = a.N / C::kFeat;
+  a.group_f = kGroupF;
+  while (tiles_f % a.group_f != 0) --a.group_f;
+  int64_t blocks = (int64_t)a.max_tiles * tiles_f * a.splits;
   blocks = (blocks + 7) / 8 * 8;  // whole XCD rounds for the remapped order
-  hipLaunchKernelGGL((tiled_gemm_kernel<BT, WT, DUAL>), dim3((unsigned)blocks), dim3(C::kThreads),
-                     0, stream, a);
+  hipLaunchKernelGGL((tiled_gemm_kernel<BT, DUAL>), dim3((unsigned)blocks),
+                     dim3(C::kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -317,7 +341,7 @@ hipError_t launch_tiled_swiglu_bf16(const void* x, const int32_t* sorted_token,
   a.E = E;
   a.P = P;
   a.splits = 1;
-  return launch_tiled<256, MOE_TILED_WT, true>(a, P, stream);
+  return launch_tiled<256, true>(a, P, stream);
 }
 
 hipError_t launch_tiled_down_bf16(const void* H, const ExpertPtrs& W2, const int32_t* offsets,
@@ -335,7 +359,7 @@ hipError_t launch_tiled_down_bf16(const void* H, const ExpertPtrs& W2, const int
   a.E = E;
   a.P = P;
   a.splits = splits;
-  return launch_tiled<256, MOE_TILED_WT, false>(a, P, stream);
+  return launch_tiled<256, false>(a, P, stream);
 }
 
 }  // namespace moe

@@ -324,3 +324,76 @@ def test_full_T512_sampled(dev):
 def test_full_prefill_T4096_sampled(dev):
     rng = np.random.default_rng(2)
     _full("prefill_bf16_T4096_zipf", dev, tokens=np.sort(rng.choice(4096, 32, replace=False)))
+
+
+# ---------------------------------------------------------------- stack (pre-norm blocks)
+def _stack_inputs(w, dev, layers):
+    blocks = []
+    for b in range(layers):
+        W_g, W1s, W3s, W2s = W.expert_weights(w, dev, block=b)
+        blocks.append((W_g, W1s, W3s, W2s))
+    h0 = W.make_x(w, blocks[0][0], dev)
+    return h0, blocks
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_stack_small_vs_oracle(dev, dtype):
+    """h <- h + MoE(RMSNorm(h)) over 4 blocks, tokens whose routing is decided
+    at every block.  Reading of the per-layer bar for a stack: every block
+    may move its own output by up to the layer tolerance (1e-2 of rms for
+    bf16, 1e-4 for fp32) and the residual stream carries each block's
+    deviation forward (RMSNorm is scale invariant, so nothing amplifies it),
+    hence max|dh| <= L x tol x rms(h); the norm-wise error must stay within
+    one layer's tolerance."""
+    layers = 4
+    tol = PY.TOL_BF16 if dtype == "bf16" else PY.TOL_F32
+    w = small(name="stack32_bf16_T4096", T=200, d=256, d_ff=256, dtype=dtype)
+    say("stack small", dtype)
+    h0, blocks = _stack_inputs(w, dev, layers)
+    h = h0.clone()
+    M.moe_stack_forward(h, blocks, w.K)
+    torch.cuda.synchronize()
+    np_blocks = [(PY.to_np(Wg), LazyNp(W1), LazyNp(W3), LazyNp(W2)) for Wg, W1, W3, W2 in blocks]
+    h_ref, margins = O.stack_forward(PY.to_np(h0), np_blocks, w.K, faithful=(dtype == "bf16"))
+    ok = np.ones(w.T, dtype=bool)
+    for m_rank, m_cut in margins:
+        ok &= m_cut > PY.DECIDED_GAP
+    assert ok.sum() > w.T // 2
+    d = PY.to_np(h)[ok] - h_ref[ok]
+    rms = np.sqrt(np.mean(h_ref[ok] ** 2))
+    max_rel = np.abs(d).max() / rms
+    l2_rel = np.sqrt(np.mean(d ** 2)) / rms
+    say("stack small %s: max %.2e, l2 %.2e of rms over %d of %d tokens decided at every block"
+        % (dtype, max_rel, l2_rel, ok.sum(), w.T))
+    assert max_rel <= layers * tol and l2_rel <= tol
+
+
+def test_full_stack32_T4096(dev):
+    """The 32-block stack at Mixtral shape (90 GB of expert weights): block 0
+    against the oracle on sampled tokens, then all 32 blocks run; the result
+    must be finite and its RMS must grow as residual sums do."""
+    w = W.WORKLOADS["stack32_bf16_T4096"]
+    say("full stack32")
+    h0, blocks = _stack_inputs(w, dev, w.layers)
+    h = h0.clone()
+    M.moe_stack_forward(h, blocks[:1], w.K)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(5).choice(w.T, 16, replace=False))
+    Wg, W1, W3, W2 = blocks[0]
+    xn_ref = O.rmsnorm(PY.to_np(h0)[rows], 1e-5, faithful=True)
+    y_ref, aux = O.moe_forward(xn_ref, PY.to_np(Wg), LazyNp(W1), LazyNp(W3), LazyNp(W2), w.K,
+                               faithful=True)
+    h1_ref = O.bf16_round(PY.to_np(h0)[rows] + y_ref)
+    ok = O.routing_margins(aux["logits"], w.K)[1] > PY.DECIDED_GAP
+    diff = np.abs(PY.to_np(h)[rows] - h1_ref)[ok]
+    rms = np.sqrt(np.mean(h1_ref ** 2))
+    say("stack32 block 0: max diff/rms %.2e over %d decided of 16" % (diff.max() / rms, ok.sum()))
+    assert np.all(diff <= 1e-2 * rms + 2.0 ** -8 * np.abs(h1_ref[ok]))
+    rms1 = h.float().pow(2).mean().sqrt().item()
+    M.moe_stack_forward(h, blocks[1:], w.K)
+    torch.cuda.synchronize()
+    assert torch.isfinite(h.float()).all()
+    rms32 = h.float().pow(2).mean().sqrt().item()
+    say("stack32 rms h0 %.3f, h1 %.3f, h32 %.3f" % (h0.float().pow(2).mean().sqrt().item(), rms1,
+                                                    rms32))
+    assert rms32 > rms1
