@@ -35,7 +35,8 @@ HEADLINE = "decode_bf16_T8"
 SWEEP = ("mid_bf16_T512", "prefill_bf16_T4096_zipf")
 DECODE_SWEEP_T = (1, 2, 4, 16, 32, 64)
 STACK = "stack32_bf16_T4096"
-STAGES = ("router_topk", "route_permute", "expert_swiglu", "expert_down", "combine")
+STAGES = ("router_topk", "route_permute", "expert_swiglu", "swiglu_finish", "expert_down",
+          "combine")
 
 
 class Layer:
@@ -78,12 +79,14 @@ class Layer:
         M.moe_route_permute(self.topk_idx, w.E, self.offsets, self.sorted_token, self.pos)
         mark(2)
         M.moe_expert_swiglu(self.x, self.W1, self.W3, w.K, self.offsets, self.sorted_token, self.H,
-                            self.scratch)
+                            self.scratch, finish=False)
         mark(3)
-        M.moe_expert_down(self.H, self.W2, w.T, w.K, self.offsets, self.O)
+        M.moe_swiglu_finish(self.scratch, w.T, w.d, w.d_ff, w.E, w.K, M.BF16, self.H)
         mark(4)
-        M.moe_combine(self.O, self.topk_w, self.pos, self.y)
+        M.moe_expert_down(self.H, self.W2, w.T, w.K, self.offsets, self.O)
         mark(5)
+        M.moe_combine(self.O, self.topk_w, self.pos, self.y)
+        mark(6)
 
     def forward_call(self):
         w = self.w
@@ -147,18 +150,47 @@ def time_layer(layer: Layer, steps: int, warmup: int):
     return wall, per_stage, wall_fwd
 
 
-def roofline_for(w, alg, per_stage_ms):
+# The W1/W3 stage is one launch of the kernel below (the split finish is a
+# separate stage); its measured HBM traffic sits in the committed counter
+# summary, keyed by kernel, workload and the sha256 of the kernel's source.
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.txt")
+CSRC = os.path.join(ROOT, "sparse_mixture_experts_32_amd", "csrc")
+SWIGLU_KERNEL = {True: ("stream_gemm_kernel<1, true>", "expert_stream_bf16.hip"),
+                 False: ("tiled_gemm_kernel<256, true>", "expert_tiled_bf16.hip")}
+
+
+def measured_traffic(workload, streaming):
+    """Calibrated FETCH+WRITE bytes per dispatch of the W1/W3 kernel, or None
+    when no row matches this workload or the kernel source changed since the
+    counters were taken."""
+    kernel, src = SWIGLU_KERNEL[bool(streaming)]
+    try:
+        import hashlib
+        sha = hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest()
+        rows = [ln.split("|") for ln in open(COUNTERS) if not ln.startswith("#") and "|" in ln]
+    except OSError:
+        return None
+    for r in rows:
+        r = [c.strip() for c in r]
+        if len(r) == 8 and r[0] == kernel and r[1] == workload and r[2] == sha:
+            return int(r[7])
+    return None
+
+
+def roofline_for(w, alg, per_stage_ms, streaming):
     g1_ms = per_stage_ms["expert_swiglu"]
     intensity = alg["swiglu_flops"] / alg["swiglu_bytes"]
+    kernel = SWIGLU_KERNEL[bool(streaming)][0]
+    traffic = measured_traffic(w.name, streaming)
     if intensity < 312:
         achieved = alg["swiglu_bytes"] / (g1_ms * 1e-3) / 1e9
-        return dict(kernel="expert_swiglu", bound="hbm", achieved=round(achieved, 1),
+        return dict(kernel=kernel, bound="hbm", achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
-                    traffic=None, avg_ms=round(g1_ms, 4))
+                    traffic=traffic, avg_ms=round(g1_ms, 4))
     achieved = alg["swiglu_flops"] / (g1_ms * 1e-3) / 1e12
-    return dict(kernel="expert_swiglu", bound="mfma", achieved=round(achieved, 1),
+    return dict(kernel=kernel, bound="mfma", achieved=round(achieved, 1),
                 peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None,
+                frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=traffic,
                 avg_ms=round(g1_ms, 4))
 
 
@@ -208,7 +240,7 @@ def run_workload(name, dev, steps, warmup):
                layer_roofline_frac=round(max(alg["layer_bytes"] / (HBM_PEAK_GBS * 1e9),
                                              alg["layer_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12))
                                          / (ms * 1e-3), 4),
-               roofline=roofline_for(w, alg, per_stage))
+               roofline=roofline_for(w, alg, per_stage, layer.plan["streaming"]))
     return res, layer
 
 
@@ -278,6 +310,17 @@ def main():
     M.load_library()
     dev = torch.device("cuda:0")
 
+    if args.only == "copy_calibration":
+        # a plain device copy of known size: what HBM counters read for it
+        # calibrates the counters of the MoE kernels
+        n = 1 << 30
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps(dict(copy_bytes_read=n, copy_bytes_written=n, calls=args.steps)))
+        return
     if args.only:
         res, _ = run_workload(args.only, dev, args.steps, args.warmup)
         print(json.dumps(res), flush=True)

@@ -113,8 +113,8 @@ moe_status moe_workspace_layout(int64_t T, int64_t d, int64_t d_ff, int32_t E, i
 
 /*
  * The whole layer: router + top-K + softmax, dispatch tables, W1/W3 SwiGLU
- * grouped GEMM, W2 grouped GEMM, gate-weighted combine -- five kernels, no
- * host synchronisation.
+ * grouped GEMM (+ the split finish for small batches), W2 grouped GEMM,
+ * gate-weighted combine -- five or six kernels, no host synchronisation.
  *   y_dtype     MOE_F32 or MOE_BF16: storage type of y.  A bf16 layer may
  *               write fp32 y (the pre-rounding sum); an fp32 layer writes fp32.
  *   accumulate  0: y = MoE(x).  1: y = round(y + MoE(x)) (residual add).
@@ -159,13 +159,23 @@ moe_status moe_route_permute(const int32_t* topk_idx, int64_t T, int32_t E, int3
  * expert e, H[r] = round(SiLU(x[sorted_token[r]] W1[e]) * (x[...] W3[e])),
  * fp32 accumulation, one rounding to dtype.  H [T*K, d_ff] in dtype.
  * scratch: device buffer of plan.swiglu_scratch_bytes (may be NULL when that
- * is 0); MOE_EWORKSPACE if smaller.  Partial sums over the K splits are added
- * in split order.
+ * is 0); MOE_EWORKSPACE if smaller.  With plan.swiglu_splits > 1 this call
+ * leaves fp32 partial sums over K slices in scratch and moe_swiglu_finish
+ * writes H; with one split it writes H itself.
  */
 moe_status moe_expert_swiglu(const void* x, const void* const* W1, const void* const* W3,
                              int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K,
                              int32_t dtype, const int32_t* offsets, const int32_t* sorted_token,
                              void* H, void* scratch, size_t scratch_bytes, void* stream);
+
+/*
+ * Completes step 6 when plan.swiglu_splits > 1 (small batches): the fp32
+ * partial sums that moe_expert_swiglu left in `scratch` are added in split
+ * order and H = round(SiLU(a) * b) is written.  With one split H is already
+ * complete and this call does nothing (MOE_OK).
+ */
+moe_status moe_swiglu_finish(const void* scratch, int64_t T, int64_t d, int64_t d_ff, int32_t E,
+                             int32_t K, int32_t dtype, void* H, void* stream);
 
 /*
  * Step 7 (code block D, second line): O_s[r] = H[r, k-slice s] W2[e][k-slice s]

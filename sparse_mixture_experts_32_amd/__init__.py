@@ -23,7 +23,8 @@ from .build import library_path
 __all__ = [
     "MoeError", "MoeLibraryMissing", "F32", "BF16", "WS_ITEMS",
     "load_library", "plan_for", "workspace_size", "workspace_layout", "moe_forward",
-    "moe_router_topk", "moe_route_permute", "moe_expert_swiglu", "moe_expert_down",
+    "moe_router_topk", "moe_route_permute", "moe_expert_swiglu", "moe_swiglu_finish",
+    "moe_expert_down",
     "moe_combine", "moe_rmsnorm", "moe_stack_forward", "EXPORTED_SYMBOLS",
 ]
 
@@ -34,7 +35,7 @@ WS_ITEMS = ("topk_idx", "topk_w", "offsets", "sorted_token", "pos", "H", "O", "s
 EXPORTED_SYMBOLS = (
     "moe_status_str", "moe_last_error", "moe_abi_version", "moe_plan_for", "moe_workspace_size",
     "moe_workspace_layout", "moe_forward", "moe_router_topk", "moe_route_permute",
-    "moe_expert_swiglu", "moe_expert_down", "moe_combine", "moe_rmsnorm",
+    "moe_expert_swiglu", "moe_swiglu_finish", "moe_expert_down", "moe_combine", "moe_rmsnorm",
 )
 
 
@@ -89,6 +90,8 @@ def load_library(path: str | None = None):
         "moe_route_permute": (_c_i32, [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p]),
         "moe_expert_swiglu": (_c_i32, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32,
                                        _c_i32, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+        "moe_swiglu_finish": (_c_i32, [_c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_p,
+                                       _c_p]),
         "moe_expert_down": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
                                      _c_p, _c_p, _c_p]),
         "moe_combine": (_c_i32, [_c_p, _c_i32, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_i32,
@@ -237,7 +240,11 @@ def moe_route_permute(topk_idx, E, offsets=None, sorted_token=None, pos=None, st
     return offsets, sorted_token, pos
 
 
-def moe_expert_swiglu(x, W1, W3, K, offsets, sorted_token, H=None, scratch=None, stream=None):
+def moe_expert_swiglu(x, W1, W3, K, offsets, sorted_token, H=None, scratch=None, stream=None,
+                      finish=True):
+    """H for every expert-sorted row.  With a K-split plan (small batches)
+    the partial sums land in ``scratch`` and, when ``finish`` is true,
+    moe_swiglu_finish completes H (pass finish=False to launch it yourself)."""
     lib = load_library()
     T, d = x.shape
     E = len(W1)
@@ -251,6 +258,15 @@ def moe_expert_swiglu(x, W1, W3, K, offsets, sorted_token, H=None, scratch=None,
     _check(lib.moe_expert_swiglu(_ptr(x), _ptr_array(W1), _ptr_array(W3), T, d, d_ff, E, K, dt,
                                  _ptr(offsets), _ptr(sorted_token), _ptr(H), _ptr(scratch),
                                  scratch.numel() if scratch is not None else 0,
+                                 _stream(stream)), lib)
+    if finish and T:
+        moe_swiglu_finish(scratch, T, d, d_ff, E, K, dt, H, stream)
+    return H
+
+
+def moe_swiglu_finish(scratch, T, d, d_ff, E, K, dtype, H, stream=None):
+    lib = load_library()
+    _check(lib.moe_swiglu_finish(_ptr(scratch), T, d, d_ff, E, K, dtype, _ptr(H),
                                  _stream(stream)), lib)
     return H
 

@@ -23,7 +23,9 @@
 //     to separate slices, summed later in slice order), so results are
 //     deterministic and the grid has thousands of workgroups.
 // Epilogue: with one split and two matrices, H = bf16(SiLU(a) * b) is
-// stored directly; otherwise the fp32 partial sums are stored.
+// stored directly; otherwise the fp32 partial sums are stored and
+// swiglu_finish_kernel (its own launch) adds the splits in order and applies
+// SwiGLU.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -274,9 +276,13 @@ hipError_t launch_stream_swiglu_bf16(const void* x, const int32_t* sorted_token,
   a.E = E;
   a.P = P;
   a.splits = splits;
-  hipError_t err = launch_stream<1, true>(a, stream);
-  if (err != hipSuccess || splits == 1) return err;
+  return launch_stream<1, true>(a, stream);
+}
+
+hipError_t launch_swiglu_finish_bf16(const float* part, int splits, int P, int d_ff, void* H,
+                                     hipStream_t stream) {
   const int64_t n4 = (int64_t)P * d_ff / 4;
+  if (n4 == 0) return hipSuccess;
   const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 2048);
   hipLaunchKernelGGL(swiglu_finish_kernel, dim3(blocks), dim3(256), 0, stream, part, splits, P,
                      d_ff, static_cast<bf16_t*>(H));

@@ -308,6 +308,21 @@ moe_status moe_expert_swiglu(const void* x, const void* const* W1, const void* c
                 "expert_swiglu");
 }
 
+moe_status moe_swiglu_finish(const void* scratch, int64_t T, int64_t d, int64_t d_ff, int32_t E,
+                             int32_t K, int32_t dtype, void* H, void* stream) {
+  moe_status s = check_shape(T, d, d_ff, E, K, dtype);
+  if (s) return s;
+  const Plan plan = make_plan(T, d, d_ff, E, K, dtype);
+  if (T == 0 || plan.swiglu_splits == 1) return ok();
+  if (!scratch || !H) return fail(MOE_EINVAL, "NULL pointer");
+  if (!aligned16(scratch) || !aligned16(H))
+    return fail(MOE_EUNSUPPORTED, "scratch and H must be 16-byte aligned");
+  return finish(moe::launch_swiglu_finish_bf16(static_cast<const float*>(scratch),
+                                               plan.swiglu_splits, (int)(T * K), (int)d_ff, H,
+                                               (hipStream_t)stream),
+                "swiglu_finish");
+}
+
 moe_status moe_expert_down(const void* H, const void* const* W2, int64_t T, int64_t d,
                            int64_t d_ff, int32_t E, int32_t K, int32_t dtype,
                            const int32_t* offsets, float* O, void* stream) {
@@ -410,6 +425,11 @@ moe_status moe_forward(const void* x, const void* W_g, const void* const* W1,
   e = run_swiglu(plan, x, sorted_token, p1, p3, offsets, P, (int)d, (int)d_ff, E, dtype, H,
                  scratch, st);
   if (e != hipSuccess) return hip_status(e, "expert_swiglu");
+  if (plan.swiglu_splits > 1) {
+    e = moe::launch_swiglu_finish_bf16(static_cast<const float*>(scratch), plan.swiglu_splits, P,
+                                       (int)d_ff, H, st);
+    if (e != hipSuccess) return hip_status(e, "swiglu_finish");
+  }
   e = run_down(plan, H, p2, offsets, P, (int)d, (int)d_ff, E, dtype, O, st);
   if (e != hipSuccess) return hip_status(e, "expert_down");
   e = moe::launch_combine(O, plan.down_splits, (int64_t)P * d, topk_w, pos, (int)T, (int)d, K, y,

@@ -43,6 +43,9 @@ hipError_t launch_stream_swiglu_bf16(const void* x, const int32_t* sorted_token,
                                      const ExpertPtrs& W1, const ExpertPtrs& W3,
                                      const int32_t* offsets, int P, int d, int d_ff, int E,
                                      int splits, float* part, void* H, hipStream_t stream);
+// H[r][f] = bf16(SiLU(sum_s part[s][0][r][f]) * sum_s part[s][1][r][f]).
+hipError_t launch_swiglu_finish_bf16(const float* part, int splits, int P, int d_ff, void* H,
+                                     hipStream_t stream);
 hipError_t launch_stream_down_bf16(const void* H, const ExpertPtrs& W2, const int32_t* offsets,
                                    int P, int d, int d_ff, int E, int splits, float* O,
                                    hipStream_t stream);
