@@ -35,6 +35,7 @@ HEADLINE = "decode_bf16_T8"
 SWEEP = ("mid_bf16_T512", "prefill_bf16_T4096_zipf")
 DECODE_SWEEP_T = (1, 2, 4, 16, 32, 64)
 STACK = "stack32_bf16_T4096"
+DECODE_STACK_T = 8
 STAGES = ("router_topk", "route_permute", "expert_swiglu", "swiglu_finish", "expert_down",
           "combine")
 
@@ -150,6 +151,30 @@ def time_layer(layer: Layer, steps: int, warmup: int):
     return wall, per_stage, wall_fwd
 
 
+FLUSH_BYTES = 1 << 30
+
+
+def time_cold(layer: Layer, steps: int):
+    """Each step timed alone with HIP events after writing a 1 GiB buffer, so
+    neither L2 nor the 256 MB Infinity Cache holds a tail of the weights from
+    the previous step.  Returns per-stage means and step percentiles (ms)."""
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=layer.x.device)
+    per = []
+    for i in range(steps):
+        flush.fill_(i & 0xFF)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
+        layer.step(evs)
+        torch.cuda.synchronize()
+        per.append([evs[j].elapsed_time(evs[j + 1]) for j in range(len(STAGES))])
+    del flush
+    per = np.asarray(per)
+    tot = per.sum(axis=1)
+    return dict(steps=steps, ms_median=round(float(np.median(tot)), 4),
+                ms_p10=round(float(np.percentile(tot, 10)), 4),
+                ms_p90=round(float(np.percentile(tot, 90)), 4),
+                stage_ms={name: round(float(per[:, j].mean()), 4) for j, name in enumerate(STAGES)})
+
+
 # The W1/W3 stage is one launch of the kernel below (the split finish is a
 # separate stage); its measured HBM traffic sits in the committed counter
 # summary, keyed by kernel, workload and the sha256 of the kernel's source.
@@ -241,6 +266,9 @@ def run_workload(name, dev, steps, warmup):
                                              alg["layer_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12))
                                          / (ms * 1e-3), 4),
                roofline=roofline_for(w, alg, per_stage, layer.plan["streaming"]))
+    cold = time_cold(layer, steps)
+    cold["roofline"] = roofline_for(w, alg, cold["stage_ms"], layer.plan["streaming"])
+    res["cold_cache"] = cold
     return res, layer
 
 
@@ -261,36 +289,82 @@ def run_decode_sweep(dev, steps, warmup):
     return out
 
 
-def run_stack(dev, steps, warmup):
-    """The 32-block stack (RMSNorm + MoE + residual per block, 90 GB of
-    expert weights resident), T = 4096 tokens per step."""
-    w = W.WORKLOADS[STACK]
-    blocks = [W.expert_weights(w, dev, block=b) for b in range(w.layers)]
-    h0 = W.make_x(w, blocks[0][0], dev)
-    h = h0.clone()
-    ws = torch.empty(M.workspace_size(w.T, w.d, w.d_ff, w.E, w.K, M.BF16), dtype=torch.uint8,
-                     device=dev)
-    xn = torch.empty_like(h)
+def _time_stack(h, h0, run, steps, warmup):
     for _ in range(warmup):
         h.copy_(h0)
-        M.moe_stack_forward(h, blocks, w.K, workspace=ws, xn=xn)
+        run()
     torch.cuda.synchronize()
     t = 0.0
     for _ in range(steps):
         h.copy_(h0)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        M.moe_stack_forward(h, blocks, w.K, workspace=ws, xn=xn)
+        run()
         torch.cuda.synchronize()
         t += time.perf_counter() - t0
-    flops = w.layers * (w.T * w.K * 6 * w.d * w.d_ff)
-    res = dict(workload=STACK, T=w.T, layers=w.layers, steps=steps,
-               ms_per_step=round(t / steps * 1e3, 3), tokens_per_s=round(w.T * steps / t, 1),
-               achieved_tflops=round(flops / (t / steps) / 1e12, 1),
-               weights_gb=round(w.layers * w.E * 3 * w.d * w.d_ff * 2 / 1e9, 1))
-    del blocks, h, h0, ws, xn
+    return t
+
+
+def run_stacks(dev, steps, warmup, decode_steps):
+    """The 32-block stack (RMSNorm + MoE + residual per block, 90 GB of
+    expert weights resident): T = 4096 tokens per step, and the same blocks
+    at T = 8 (decode through all 32 blocks, eager and replayed from a HIP
+    graph that holds the whole step)."""
+    w = W.WORKLOADS[STACK]
+    blocks = [W.expert_weights(w, dev, block=b) for b in range(w.layers)]
+    weights_gb = w.layers * w.E * 3 * w.d * w.d_ff * 2 / 1e9
+    out = []
+    for T in (w.T, DECODE_STACK_T):
+        h0 = W.make_x(w, blocks[0][0], dev, T=T)
+        h = h0.clone()
+        ws = torch.empty(M.workspace_size(T, w.d, w.d_ff, w.E, w.K, M.BF16), dtype=torch.uint8,
+                         device=dev)
+        xn = torch.empty_like(h)
+
+        def run():
+            M.moe_stack_forward(h, blocks, w.K, workspace=ws, xn=xn)
+
+        t = _time_stack(h, h0, run, steps if T == w.T else decode_steps, warmup)
+        n = steps if T == w.T else decode_steps
+        ms = t / n * 1e3
+        res = dict(workload="stack32_bf16_T%d" % T, T=T, layers=w.layers, steps=n,
+                   ms_per_step=round(ms, 3), tokens_per_s=round(T / (ms * 1e-3), 1),
+                   weights_gb=round(weights_gb, 1))
+        if T == w.T:
+            flops = w.layers * (T * w.K * 6 * w.d * w.d_ff)
+            res["achieved_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+            res["mfma_frac"] = round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+        else:
+            # experts that received tokens, block by block (untimed pass)
+            views = M.workspace_views(ws, T, w.d, w.d_ff, w.E, w.K, M.BF16)
+            h.copy_(h0)
+            n_active = []
+            for blk in blocks:
+                M.moe_stack_forward(h, [blk], w.K, workspace=ws, xn=xn)
+                n_active.append(int((views["offsets"].diff() > 0).sum().item()))
+            alg = sum(n_active) * 3 * w.d * w.d_ff * 2 + w.layers * (
+                w.d * w.E * 2 + 3 * T * w.d * 2)
+            res["n_active_per_block"] = n_active
+            res["algorithmic_bytes"] = alg
+            res["hbm_frac"] = round(alg / (HBM_PEAK_GBS * 1e9) / (ms * 1e-3), 4)
+            # the whole step captured once and replayed
+            g = torch.cuda.CUDAGraph()
+            h.copy_(h0)
+            run()                      # warm (first-use attributes set outside the capture)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                run()
+            tg = _time_stack(h, h0, g.replay, decode_steps, warmup)
+            msg = tg / decode_steps * 1e3
+            res["graph_ms_per_step"] = round(msg, 3)
+            res["graph_tokens_per_s"] = round(T / (msg * 1e-3), 1)
+            res["graph_hbm_frac"] = round(alg / (HBM_PEAK_GBS * 1e9) / (msg * 1e-3), 4)
+            del g
+        out.append(res)
+        del h, h0, ws, xn
+    del blocks
     torch.cuda.empty_cache()
-    return res
+    return out
 
 
 def main():
@@ -342,9 +416,9 @@ def main():
             del lay
             torch.cuda.empty_cache()
     decode_sweep = [] if args.no_sweep else run_decode_sweep(dev, max(5, args.steps // 5), 2)
-    stack = None if (args.no_sweep or args.no_stack) else run_stack(dev, 3, 1)
-    if stack:
-        print("# %s done: %.1f ms/step" % (STACK, stack["ms_per_step"]), file=sys.stderr,
+    stack = None if (args.no_sweep or args.no_stack) else run_stacks(dev, 3, 1, 10)
+    for r in stack or []:
+        print("# %s done: %.1f ms/step" % (r["workload"], r["ms_per_step"]), file=sys.stderr,
               flush=True)
     w = W.WORKLOADS[HEADLINE]
     out = {

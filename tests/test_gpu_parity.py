@@ -368,6 +368,36 @@ def test_stack_small_vs_oracle(dev, dtype):
     assert max_rel <= layers * tol and l2_rel <= tol
 
 
+def test_stack_graph_replay_matches_eager(dev):
+    """The whole decode-size stack step captured in one HIP graph: every
+    replay, with eager work and synchronisations between replays, gives the
+    eager result bit for bit (the library allocates and memsets nothing, so
+    the captured step is only its kernels)."""
+    w = small(name="stack32_bf16_T4096", T=8, d=256, d_ff=512, dtype="bf16")
+    say("stack graph replay")
+    h0, blocks = _stack_inputs(w, dev, 3)
+    ws = torch.empty(M.workspace_size(w.T, w.d, w.d_ff, w.E, w.K, M.BF16), dtype=torch.uint8,
+                     device=dev)
+    h = h0.clone()
+    xn = torch.empty_like(h)
+    M.moe_stack_forward(h, blocks, w.K, workspace=ws, xn=xn)
+    torch.cuda.synchronize()
+    eager = h.clone()
+    g = torch.cuda.CUDAGraph()
+    h.copy_(h0)
+    with torch.cuda.graph(g):
+        M.moe_stack_forward(h, blocks, w.K, workspace=ws, xn=xn)
+    for rep in range(4):
+        h.copy_(h0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(h, eager), "replay %d" % rep
+        # eager work between replays that reuses the same workspace
+        h.copy_(h0)
+        M.moe_stack_forward(h, blocks[:1], w.K, workspace=ws, xn=xn)
+        torch.cuda.synchronize()
+
+
 def test_full_stack32_T4096(dev):
     """The 32-block stack at Mixtral shape (90 GB of expert weights): block 0
     against the oracle on sampled tokens, then all 32 blocks run; the result
