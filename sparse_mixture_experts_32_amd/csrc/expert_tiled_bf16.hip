@@ -25,11 +25,19 @@
 //     wave's matrix instructions cover the other's LDS reads),
 //     v_mfma_f32_16x16x32_bf16 with fp32 accumulators; D is
 //     [feature][token], so the epilogue writes 4 consecutive features per
-//     lane (SiLU(a) * b fused for W1/W3); token groups of a wave that lie
-//     wholly in the padding of an expert's last tile skip their multiplies;
+//     lane (SiLU(a) * b fused for W1/W3);
+//   * per k-stage a wave reads its fragments, then its 32 matrix instructions
+//     run with the stage's four load issues spread between them (one after
+//     every 8), so the vector-memory queue drains while the matrix cores
+//     work instead of stalling the wave right after the barrier; the k loop
+//     is instantiated twice -- one straight block for tiles whose token
+//     groups are all live, one that skips the groups lying wholly in the
+//     padding of an expert's last tile;
 //   * tile order: each XCD runs a contiguous range in which 4 feature tiles
 //     are interleaved with the token tiles, so the ~32 workgroups it runs at
 //     once share a few weight tiles and a few token tiles in its L2.
+#include <type_traits>
+
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -218,30 +226,53 @@ __global__ __launch_bounds__(128 * kWavesT) void tiled_gemm_kernel(TiledArgs arg
     for (int jb = 0; jb < C::kNJ; ++jb) acc[i][jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   bf16x8_t fa[C::kMI], fb[C::kNJ];
-  auto read_frags = [&](const char* w_src, const char* a_src) {
+  auto read_fa = [&](int i, const char* w_src) {
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t*)((lds_char_t*)w_src + a_off[i][0]));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t*)((lds_char_t*)w_src + a_off[i][1]));
+    const s16x4_t both[2] = {lo, hi};
+    fa[i] = __builtin_bit_cast(bf16x8_t, both);
+  };
+  auto read_fb = [&](const char* a_src) {
 #pragma unroll
     for (int jb = 0; jb < C::kNJ; ++jb)
       fb[jb] = *reinterpret_cast<const bf16x8_t*>(a_src + b_off[jb]);
+  };
+  auto read_frags = [&](const char* w_src, const char* a_src) {
+    read_fb(a_src);
 #pragma unroll
-    for (int i = 0; i < C::kMI; ++i) {
-      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4_t*)((lds_char_t*)w_src + a_off[i][0]));
-      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4_t*)((lds_char_t*)w_src + a_off[i][1]));
-      const s16x4_t both[2] = {lo, hi};
-      fa[i] = __builtin_bit_cast(bf16x8_t, both);
-    }
+    for (int i = 0; i < C::kMI; ++i) read_fa(i, w_src);
   };
   // Token groups of the wave that lie wholly past the expert's segment (the
   // padding of its last tile) are skipped: their outputs are never stored.
   const int live_groups = min(C::kNJ, (row_end - row_begin - wt * C::kWT + 15) / 16);
-  auto mma = [&]() {
-#pragma unroll
-    for (int jb = 0; jb < C::kNJ; ++jb) {
-      if (jb >= live_groups) break;
+  // FULL: every token group of the wave is live (all tiles but the last of
+  // an expert), so the 32 matrix instructions form one straight block and a
+  // load issue can go after every 8 of them; otherwise dead groups are skipped.
+  auto mma = [&](auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    if constexpr (FULL) {
+      // weight fragment outer: the first multiplies need only fb[] and fa[0]
 #pragma unroll
       for (int i = 0; i < C::kMI; ++i)
-        acc[i][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[jb], acc[i][jb], 0, 0, 0);
+#pragma unroll
+        for (int jb = 0; jb < C::kNJ; ++jb)
+          acc[i][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[jb], acc[i][jb], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::kMI + C::kNJ, 0);   // ds reads first
+#pragma unroll
+      for (int q = 0; q < C::kDmaPerStage; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // 8 matrix instructions
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one load issue
+      }
+    } else {
+#pragma unroll
+      for (int jb = 0; jb < C::kNJ; ++jb) {
+        if (jb >= live_groups) break;
+#pragma unroll
+        for (int i = 0; i < C::kMI; ++i)
+          acc[i][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[jb], acc[i][jb], 0, 0, 0);
+      }
     }
   };
 
@@ -253,20 +284,26 @@ __global__ __launch_bounds__(128 * kWavesT) void tiled_gemm_kernel(TiledArgs arg
 #pragma unroll
   for (int s = 0; s < kSlots - 1; ++s) issue(s, sW[s], sA[s]);
 
-  for (int k0 = 0; k0 < nk; k0 += kSlots) {
+  auto k_loop = [&](auto full_tag) {
+    for (int k0 = 0; k0 < nk; k0 += kSlots) {
 #pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
-      const int kt = k0 + s;
-      wait_vm<(kSlots - 2) * C::kDmaPerStage>();   // stage kt landed; later ones may not have
-      __builtin_amdgcn_s_barrier();                // ... for every wave; slot of kt-1 is free
-      // read this slot's operands, then refill the slot every wave finished
-      // reading in the previous stage, then multiply
-      read_frags(sW[s], sA[s]);
-      issue(min(kt + kSlots - 1, nk - 1), sW[(s + kSlots - 1) % kSlots],
-            sA[(s + kSlots - 1) % kSlots]);
-      mma();
+      for (int s = 0; s < kSlots; ++s) {
+        const int kt = k0 + s;
+        wait_vm<(kSlots - 2) * C::kDmaPerStage>();   // stage kt landed; later ones may not have
+        __builtin_amdgcn_s_barrier();                // ... for every wave; slot of kt-1 is free
+        // read this slot's operands, refill the slot every wave finished
+        // reading in the previous stage, multiply
+        read_frags(sW[s], sA[s]);
+        issue(min(kt + kSlots - 1, nk - 1), sW[(s + kSlots - 1) % kSlots],
+              sA[(s + kSlots - 1) % kSlots]);
+        mma(full_tag);
+      }
     }
-  }
+  };
+  if (live_groups == C::kNJ)
+    k_loop(std::true_type{});
+  else
+    k_loop(std::false_type{});
   wait_vm<0>();  // no load may land in LDS after the workgroup ends
 
   // ---- epilogue: lane holds features f .. f+3 of token column j ----
