@@ -15,7 +15,10 @@
 //     features of k-row (i / 4), and lane j receives element j % 4 of lanes
 //     j / 4 + 4q, i.e. 4 consecutive k of one feature;
 //   * 16-byte chunks are XOR-swizzled per row so the transposed reads and
-//     the token-operand reads are free of LDS bank conflicts;
+//     the token-operand reads are free of LDS bank conflicts (the token
+//     swizzle, chunk ^ (row / 2) mod 4 over 64-byte rows, is the one that
+//     gfx950's bank-conflict counter reads as zero for the 16-row operand
+//     read; (row / 4) mod 4 is 2-way conflicted there);
 //   * each slot is its own __shared__ object and the k loop is unrolled over
 //     the four slots, so the compiler can prove a slot's reads independent of
 //     the loads in flight to the other slots; waits are explicit vmcnt counts
@@ -78,7 +81,7 @@ struct TiledArgs {
 
 // Chunk swizzles (16-byte chunks): weight rows hold 32 chunks, token rows 4.
 __device__ __forceinline__ int swz_w(int r) { return 2 * (r & 3) + 8 * ((r >> 3) & 1); }
-__device__ __forceinline__ int swz_a(int t) { return (t >> 2) & 3; }
+__device__ __forceinline__ int swz_a(int t) { return (t >> 1) & 3; }
 
 __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds((global_void_t*)src, (lds_void_t*)lds_dst, 16, 0, 0);
