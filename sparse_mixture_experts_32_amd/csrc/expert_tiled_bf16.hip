@@ -30,8 +30,8 @@
 //     [feature][token], so the epilogue writes 4 consecutive features per
 //     lane (SiLU(a) * b fused for W1/W3);
 //   * per k-stage a wave reads its fragments, then its 32 matrix instructions
-//     run with the stage's four load issues spread between them (one after
-//     every 8), so the vector-memory queue drains while the matrix cores
+//     run with the stage's four load issues spread between them (one ahead
+//     of every 8), so the vector-memory queue drains while the matrix cores
 //     work instead of stalling the wave right after the barrier; the k loop
 //     is instantiated twice -- one straight block for tiles whose token
 //     groups are all live, one that skips the groups lying wholly in the
@@ -262,11 +262,12 @@ __global__ __launch_bounds__(128 * kWavesT) void tiled_gemm_kernel(TiledArgs arg
 #pragma unroll
         for (int jb = 0; jb < C::kNJ; ++jb)
           acc[i][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[jb], acc[i][jb], 0, 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::kMI + C::kNJ, 0);   // ds reads first
+      // ds reads first, then each load issue ahead of 8 matrix instructions
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::kMI + C::kNJ, 0);
 #pragma unroll
       for (int q = 0; q < C::kDmaPerStage; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // 8 matrix instructions
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one load issue
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // 8 matrix instructions
       }
     } else {
 #pragma unroll
