@@ -1,4 +1,5 @@
-"""CPU oracle for the Mixtral sparse mixture-of-experts layer forward.
+"""CPU oracle for the Mixtral sparse mixture-of-experts layer forward and the
+attention sub-block in front of it.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or
 links this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
@@ -10,4 +11,7 @@ Modules
 -------
 ``moe_oracle``  numpy float64 implementation of the layer, for every size.
 ``scalar``      pure-Python loops over the definition, for tiny shapes.
+``swa_oracle``  float64 sliding-window grouped-query attention with the
+                rolling-buffer cache and chunked prefill (the sub-block in
+                front of the MoE).
 """
