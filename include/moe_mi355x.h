@@ -206,6 +206,62 @@ moe_status moe_combine(const float* O, int32_t o_splits, const float* topk_w, co
 moe_status moe_rmsnorm(const void* h, void* out, int64_t T, int64_t d, float eps, int32_t dtype,
                        void* stream);
 
+/* ------------------------------------------------------------------------
+ * The attention sub-block in front of the MoE ("从Mistral 7B到MoE模型Mixtral
+ * 8x7B的全面解析", aiqianji.com, sections 1.1 and 1.2.1-1.2.3):
+ * grouped-query attention over a sliding window of W positions, with a
+ * rolling-buffer key/value cache and chunked prefill.
+ *
+ *   position of query token t of sequence b:   p = pos0[b] + t
+ *   keys it attends to:                         positions max(0, p-W+1) .. p
+ *   key/value head of query head h:             h / (n_heads / n_kv_heads)
+ *   weights:                                    softmax over those keys of
+ *                                               q.k / sqrt(head_dim)
+ *   output:                                     sum of weight * v
+ *
+ * Layout (row-major, bf16):
+ *   q                  [B, T, n_heads, head_dim]
+ *   k_new, v_new       [B, T, n_kv_heads, head_dim]   the chunk's keys/values
+ *   k_cache, v_cache   [B, W, n_kv_heads, head_dim]   rolling buffer (section
+ *                      1.2.2): position j lives in slot j mod W
+ *   pos0               [B] int32, device: position of the chunk's first token
+ *   out                [B, T, n_heads, head_dim], bf16 or fp32 (out_dtype)
+ * Supported: head_dim = 128; n_heads / n_kv_heads in {1, 2, 4}; 1 <= T <= W
+ * (the pages chunk prompts by the window size).  T = 0 or B = 0 is a no-op.
+ *
+ * Contract on the device data: a key at position j < pos0[b] is read from
+ * the cache slot j mod W, so the cache must hold positions
+ * max(0, pos0[b] - W + 1) .. pos0[b] - 1 (every earlier chunk appended with
+ * swa_cache_append, in order); keys at positions >= pos0[b] come from
+ * k_new / v_new.  Attention reads the cache as it stands; append the chunk
+ * after the attention call (section 1.2.3).
+ * ---------------------------------------------------------------------- */
+
+/* Workspace bytes swa_attention needs for this shape (0 when the key range
+ * is not split over workgroups). */
+moe_status swa_workspace_size(int64_t B, int64_t T, int64_t W, int32_t n_heads,
+                              int32_t n_kv_heads, int32_t head_dim, size_t* bytes);
+
+/* One chunk of sliding-window grouped-query attention (sections 1.1, 1.2.1,
+ * 1.2.3).  workspace: device buffer of swa_workspace_size bytes, 256-byte
+ * aligned (may be NULL when that is 0).  All pointers 16-byte aligned; out
+ * may not overlap q, k_new, v_new or the cache. */
+moe_status swa_attention(const void* q, const void* k_new, const void* v_new,
+                         const void* k_cache, const void* v_cache, const int32_t* pos0,
+                         int64_t B, int64_t T, int64_t W, int32_t n_heads, int32_t n_kv_heads,
+                         int32_t head_dim, void* out, int32_t out_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Rolling-buffer append (section 1.2.2): the keys and values of position
+ * pos0[b] + t are written to slot (pos0[b] + t) mod W of sequence b's cache,
+ * for the last min(T, W) tokens of the chunk (earlier ones would be
+ * overwritten by later ones of the same chunk).  k_new, v_new
+ * [B, T, n_kv_heads, head_dim]; k_cache, v_cache [B, W, n_kv_heads, head_dim];
+ * bf16, 16-byte aligned; T >= 1 (any T; T = 0 is a no-op). */
+moe_status swa_cache_append(const void* k_new, const void* v_new, const int32_t* pos0,
+                            int64_t B, int64_t T, int64_t W, int32_t n_kv_heads, int32_t head_dim,
+                            void* k_cache, void* v_cache, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

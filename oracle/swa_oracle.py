@@ -105,14 +105,15 @@ def swa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, W: int) -> np.nda
 
 def swa_chunk_attention(q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
                         k_cache: np.ndarray, v_cache: np.ndarray, pos0: int,
-                        W: int) -> np.ndarray:
+                        W: int, rows=None) -> np.ndarray:
     """One chunk of T <= W tokens at positions pos0 .. pos0+T-1 of one
     sequence, given the rolling cache as it stands before the chunk
     (*全面解析* section 1.2.3): a key at position p < pos0 is read from cache
     slot p mod W, a key at p >= pos0 from the chunk row p - pos0.
 
     q [T, H, hd]; k_new, v_new [T, KVH, hd]; k_cache, v_cache [W, KVH, hd].
-    Returns o [T, H, hd] float64."""
+    ``rows`` picks the chunk tokens to compute (default: all).
+    Returns o [len(rows), H, hd] float64."""
     q = np.asarray(q, dtype=np.float64)
     k_new = np.asarray(k_new, dtype=np.float64)
     v_new = np.asarray(v_new, dtype=np.float64)
@@ -122,8 +123,9 @@ def swa_chunk_attention(q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
     KVH = k_new.shape[1]
     if T > W:
         raise ValueError("a chunk is at most W tokens long")
-    out = np.zeros((T, H, hd))
-    for t in range(T):
+    rows = range(T) if rows is None else list(rows)
+    out = np.zeros((len(rows), H, hd))
+    for n, t in enumerate(rows):
         p = pos0 + t
         pos = list(window_keys(p, W))
         keys = np.stack([k_cache[rolling_slot(j, W)] if j < pos0 else k_new[j - pos0]
@@ -132,7 +134,7 @@ def swa_chunk_attention(q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
                          for j in pos])
         for h in range(H):
             g = kv_head_of(h, H, KVH)
-            out[t, h] = _attend(q[t, h], keys[:, g], vals[:, g])
+            out[n, h] = _attend(q[t, h], keys[:, g], vals[:, g])
     return out
 
 

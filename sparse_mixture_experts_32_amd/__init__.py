@@ -26,6 +26,7 @@ __all__ = [
     "moe_router_topk", "moe_route_permute", "moe_expert_swiglu", "moe_swiglu_finish",
     "moe_expert_down",
     "moe_combine", "moe_rmsnorm", "moe_stack_forward", "EXPORTED_SYMBOLS",
+    "swa_workspace_size", "swa_attention", "swa_cache_append",
 ]
 
 F32 = 0
@@ -36,6 +37,7 @@ EXPORTED_SYMBOLS = (
     "moe_status_str", "moe_last_error", "moe_abi_version", "moe_plan_for", "moe_workspace_size",
     "moe_workspace_layout", "moe_forward", "moe_router_topk", "moe_route_permute",
     "moe_expert_swiglu", "moe_swiglu_finish", "moe_expert_down", "moe_combine", "moe_rmsnorm",
+    "swa_workspace_size", "swa_attention", "swa_cache_append",
 )
 
 
@@ -97,6 +99,12 @@ def load_library(path: str | None = None):
         "moe_combine": (_c_i32, [_c_p, _c_i32, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_i32,
                                  _c_i32, _c_p]),
         "moe_rmsnorm": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, ctypes.c_float, _c_i32, _c_p]),
+        "swa_workspace_size": (_c_i32, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
+                                        ctypes.POINTER(_c_sz)]),
+        "swa_attention": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64,
+                                   _c_i32, _c_i32, _c_i32, _c_p, _c_i32, _c_p, _c_sz, _c_p]),
+        "swa_cache_append": (_c_i32, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32,
+                                      _c_p, _c_p, _c_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -327,3 +335,50 @@ def moe_stack_forward(h, blocks, K, eps=1e-5, workspace=None, xn=None, stream=No
         moe_forward(xn, W_g, W1s, W3s, W2s, K, y=h, accumulate=True, workspace=workspace,
                     stream=stream)
     return h
+
+
+# ---------------------------------------------------------------------------
+# Attention sub-block: sliding-window grouped-query attention with a
+# rolling-buffer cache ("从Mistral 7B到MoE模型Mixtral 8x7B的全面解析",
+# aiqianji.com, sections 1.1 and 1.2.1-1.2.3).
+
+def swa_workspace_size(B, T, W, n_heads, n_kv_heads, head_dim=128) -> int:
+    lib = load_library()
+    n = _c_sz()
+    _check(lib.swa_workspace_size(B, T, W, n_heads, n_kv_heads, head_dim, ctypes.byref(n)), lib)
+    return n.value
+
+
+def swa_attention(q, k_new, v_new, k_cache, v_cache, pos0, W, out=None, out_dtype=None,
+                  workspace=None, stream=None):
+    """Attention of one chunk: q [B, T, H, hd], k_new/v_new [B, T, KVH, hd],
+    caches [B, W, KVH, hd] (bf16), pos0 [B] int32 (device).  The cache is read
+    as it stands; call ``swa_cache_append`` afterwards.  Returns out
+    [B, T, H, hd] (bf16, or fp32 with out_dtype=torch.float32)."""
+    lib = load_library()
+    B, T, H, hd = q.shape
+    KVH = k_new.shape[2]
+    if pos0.dtype != torch.int32:
+        raise TypeError("pos0 must be int32")
+    if out is None:
+        out = torch.empty((B, T, H, hd), dtype=out_dtype or q.dtype, device=q.device)
+    need = swa_workspace_size(B, T, W, H, KVH, hd)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib.swa_attention(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                             _ptr(pos0), B, T, W, H, KVH, hd, _ptr(out), _dtype_code(out),
+                             _ptr(workspace) if need else None,
+                             workspace.numel() if (need and workspace is not None) else 0,
+                             _stream(stream)), lib)
+    return out
+
+
+def swa_cache_append(k_new, v_new, pos0, k_cache, v_cache, stream=None):
+    """Write the chunk's keys and values into the rolling buffer, position p
+    to slot p mod W (section 1.2.2)."""
+    lib = load_library()
+    B, T, KVH, hd = k_new.shape
+    W = k_cache.shape[1]
+    _check(lib.swa_cache_append(_ptr(k_new), _ptr(v_new), _ptr(pos0), B, T, W, KVH, hd,
+                                _ptr(k_cache), _ptr(v_cache), _stream(stream)), lib)
+    return k_cache, v_cache

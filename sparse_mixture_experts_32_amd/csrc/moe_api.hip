@@ -438,4 +438,106 @@ moe_status moe_forward(const void* x, const void* W_g, const void* const* W1,
   return ok();
 }
 
+// ---- attention sub-block ----
+
+namespace {
+
+moe_status swa_check(int64_t B, int64_t T, int64_t W, int32_t H, int32_t KVH, int32_t hd) {
+  if (B < 0 || T < 0) return fail(MOE_EINVAL, "B and T must be >= 0");
+  if (W < 1 || W >= (int64_t(1) << 30)) return fail(MOE_EINVAL, "W = %lld out of range", (long long)W);
+  if (H < 1 || KVH < 1 || H % KVH != 0)
+    return fail(MOE_EINVAL, "n_heads must be a positive multiple of n_kv_heads");
+  if (hd != moe::swa_head_dim()) return fail(MOE_EUNSUPPORTED, "head_dim must be 128");
+  const int32_t G = H / KVH;
+  if (G != 1 && G != 2 && G != 4)
+    return fail(MOE_EUNSUPPORTED, "n_heads / n_kv_heads = %d, supported 1, 2, 4", G);
+  if (T > W) return fail(MOE_EUNSUPPORTED, "a chunk is at most W tokens (T = %lld, W = %lld)",
+                         (long long)T, (long long)W);
+  if (B * T * H * hd >= (int64_t(1) << 31) || B * W * KVH * hd >= (int64_t(1) << 40))
+    return fail(MOE_EUNSUPPORTED, "shape too large");
+  return MOE_OK;
+}
+
+size_t swa_ws_bytes(int64_t B, int64_t T, int64_t W, int32_t H, int32_t KVH) {
+  const int splits = moe::swa_plan_splits((int)B, (int)T, (int)W, H, KVH, nullptr, nullptr);
+  if (splits <= 1 || B == 0 || T == 0) return 0;
+  const size_t rows = (size_t)B * T * H * splits;
+  const size_t o = (rows * 128 * sizeof(float) + 255) / 256 * 256;
+  return o + rows * 2 * sizeof(float);
+}
+
+}  // namespace
+
+moe_status swa_workspace_size(int64_t B, int64_t T, int64_t W, int32_t n_heads,
+                              int32_t n_kv_heads, int32_t head_dim, size_t* bytes) {
+  if (!bytes) return fail(MOE_EINVAL, "bytes is NULL");
+  moe_status s = swa_check(B, T, W, n_heads, n_kv_heads, head_dim);
+  if (s) return s;
+  *bytes = swa_ws_bytes(B, T, W, n_heads, n_kv_heads);
+  return ok();
+}
+
+moe_status swa_attention(const void* q, const void* k_new, const void* v_new,
+                         const void* k_cache, const void* v_cache, const int32_t* pos0,
+                         int64_t B, int64_t T, int64_t W, int32_t n_heads, int32_t n_kv_heads,
+                         int32_t head_dim, void* out, int32_t out_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  moe_status s = swa_check(B, T, W, n_heads, n_kv_heads, head_dim);
+  if (s) return s;
+  s = check_dtype(out_dtype, "out_dtype");
+  if (s) return s;
+  if (B == 0 || T == 0) return ok();
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !pos0 || !out)
+    return fail(MOE_EINVAL, "NULL pointer");
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(out))
+    return fail(MOE_EUNSUPPORTED, "q, k_new, v_new, caches and out must be 16-byte aligned");
+  const size_t qbytes = (size_t)B * T * n_heads * head_dim * 2;
+  const size_t obytes = (size_t)B * T * n_heads * head_dim * (out_dtype == MOE_F32 ? 4 : 2);
+  const size_t nbytes = (size_t)B * T * n_kv_heads * head_dim * 2;
+  const size_t cbytes = (size_t)B * W * n_kv_heads * head_dim * 2;
+  if (overlap(out, obytes, q, qbytes) || overlap(out, obytes, k_new, nbytes) ||
+      overlap(out, obytes, v_new, nbytes) || overlap(out, obytes, k_cache, cbytes) ||
+      overlap(out, obytes, v_cache, cbytes))
+    return fail(MOE_EINVAL, "out overlaps an input");
+  const size_t need = swa_ws_bytes(B, T, W, n_heads, n_kv_heads);
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(MOE_EWORKSPACE, "workspace has %zu bytes, needs %zu",
+                  workspace ? workspace_bytes : 0, need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(MOE_EWORKSPACE, "workspace must be 256-byte aligned");
+    const int splits = moe::swa_plan_splits((int)B, (int)T, (int)W, n_heads, n_kv_heads,
+                                            nullptr, nullptr);
+    const size_t rows = (size_t)B * T * n_heads * splits;
+    part_o = static_cast<float*>(workspace);
+    part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       (rows * 128 * sizeof(float) + 255) / 256 * 256);
+  }
+  return finish(moe::launch_swa_attention(q, k_new, v_new, k_cache, v_cache, pos0, (int)B,
+                                          (int)T, (int)W, n_heads, n_kv_heads, out,
+                                          out_dtype == MOE_F32 ? 1 : 0, part_o, part_ml,
+                                          (hipStream_t)stream),
+                "swa_attention");
+}
+
+moe_status swa_cache_append(const void* k_new, const void* v_new, const int32_t* pos0,
+                            int64_t B, int64_t T, int64_t W, int32_t n_kv_heads, int32_t head_dim,
+                            void* k_cache, void* v_cache, void* stream) {
+  if (B < 0 || T < 0) return fail(MOE_EINVAL, "B and T must be >= 0");
+  if (W < 1 || W >= (int64_t(1) << 30)) return fail(MOE_EINVAL, "W out of range");
+  if (n_kv_heads < 1) return fail(MOE_EINVAL, "n_kv_heads must be >= 1");
+  if (head_dim != moe::swa_head_dim()) return fail(MOE_EUNSUPPORTED, "head_dim must be 128");
+  if (B == 0 || T == 0) return ok();
+  if (!k_new || !v_new || !pos0 || !k_cache || !v_cache) return fail(MOE_EINVAL, "NULL pointer");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(MOE_EUNSUPPORTED, "keys, values and caches must be 16-byte aligned");
+  if (B * T * n_kv_heads * head_dim >= (int64_t(1) << 40)) return fail(MOE_EUNSUPPORTED, "too large");
+  return finish(moe::launch_swa_append(k_new, v_new, pos0, (int)B, (int)T, (int)W, n_kv_heads,
+                                       k_cache, v_cache, (hipStream_t)stream),
+                "swa_cache_append");
+}
+
 }  // extern "C"

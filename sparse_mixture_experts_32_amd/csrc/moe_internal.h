@@ -75,4 +75,15 @@ hipError_t launch_combine(const float* O, int o_splits, int64_t slice, const flo
 hipError_t launch_rmsnorm(const void* h, void* out, int T, int d, float eps, int dtype,
                           hipStream_t stream);
 
+// Sliding-window grouped-query attention (swa_attention.hip).
+int swa_head_dim();
+int swa_plan_splits(int B, int T, int W, int H, int KVH, int* qtiles_out, int* qsub_out);
+hipError_t launch_swa_attention(const void* q, const void* k_new, const void* v_new,
+                                const void* k_cache, const void* v_cache, const int32_t* pos0,
+                                int B, int T, int W, int H, int KVH, void* out, int out_f32,
+                                float* part_o, float* part_ml, hipStream_t stream);
+hipError_t launch_swa_append(const void* k_new, const void* v_new, const int32_t* pos0, int B,
+                             int T, int W, int KVH, void* k_cache, void* v_cache,
+                             hipStream_t stream);
+
 }  // namespace moe

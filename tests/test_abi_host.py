@@ -31,7 +31,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:moe|swa)_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_binding_symbols():
@@ -145,3 +145,41 @@ def test_stage_entry_points_validate(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(M.MoeLibraryMissing):
         M.load_library(str(tmp_path / "missing.so"))
+
+
+def _swa(lib, B=1, T=4, W=16, H=8, KVH=2, hd=128, q=FAKE, kn=FAKE + 0x100000, vn=FAKE + 0x200000,
+         kc=FAKE + 0x300000, vc=FAKE + 0x400000, pos=FAKE + 0x500000, out=FAKE2, odt=1,
+         ws=None, ws_bytes=0):
+    return lib.swa_attention(q, kn, vn, kc, vc, pos, B, T, W, H, KVH, hd, out, odt, ws, ws_bytes,
+                             None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(q=None), EINVAL),
+    (dict(pos=None), EINVAL),
+    (dict(out=None), EINVAL),
+    (dict(B=-1), EINVAL),
+    (dict(W=0), EINVAL),
+    (dict(H=6, KVH=4), EINVAL),                 # not a multiple
+    (dict(H=16, KVH=2), EUNSUPPORTED),          # group of 8
+    (dict(hd=64), EUNSUPPORTED),
+    (dict(T=17, W=16), EUNSUPPORTED),           # chunk longer than the window
+    (dict(odt=7), EINVAL),
+    (dict(q=FAKE + 8), EUNSUPPORTED),           # misaligned
+    (dict(out=FAKE), EINVAL),                   # out overlaps q
+    (dict(B=8, T=1, W=4096, H=32, KVH=8), EWORKSPACE),   # key splits need a workspace
+])
+def test_swa_attention_rejects_before_launch(lib, kwargs, status):
+    got = _swa(lib, **kwargs)
+    assert got == status, lib.moe_last_error()
+    assert lib.moe_last_error() != b""
+
+
+def test_swa_noops_and_workspace_size(lib):
+    assert _swa(lib, T=0) == OK and _swa(lib, B=0) == OK
+    assert M.swa_workspace_size(1, 4096, 4096, 32, 8) == 0        # prefill: no key splits
+    n = M.swa_workspace_size(8, 1, 4096, 32, 8)                   # decode: split keys
+    assert n >= 8 * 32 * 2 * (128 + 2) * 4
+    assert lib.swa_cache_append(FAKE, FAKE, FAKE, 1, 0, 16, 2, 128, FAKE2, FAKE2, None) == OK
+    assert lib.swa_cache_append(FAKE, FAKE, FAKE, 1, 4, 16, 2, 64, FAKE2, FAKE2, None) == EUNSUPPORTED
+    assert lib.swa_cache_append(None, FAKE, FAKE, 1, 4, 16, 2, 128, FAKE2, FAKE2, None) == EINVAL

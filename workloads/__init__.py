@@ -175,3 +175,48 @@ def sha256_of(tensors) -> str:
     for t in tensors:
         h.update(t.detach().contiguous().view(torch.uint8).cpu().numpy().tobytes())
     return h.hexdigest()
+
+
+# ---------------------------------------------------------------------------
+# Attention sub-block (sliding-window grouped-query attention with a rolling
+# cache): seeded synthetic chunks.  q, k, v ~ N(0, 1) rounded to bf16, so the
+# scaled scores q.k / sqrt(128) are ~N(0, 1); the cache is filled with N(0, 1)
+# rows (any slot content is a possible history: only the slots of the last
+# W - 1 positions before pos0 are ever read).
+
+@dataclass(frozen=True)
+class AttnWorkload:
+    name: str
+    B: int
+    T: int
+    W: int
+    H: int
+    KVH: int
+    pos0: tuple
+    seed: int
+    hd: int = 128
+
+
+ATTN_WORKLOADS = {
+    # decode: 8 sequences, one new token each, cache wrapped (position 8191 > W)
+    "attn_decode_bf16_B8": AttnWorkload("attn_decode_bf16_B8", 8, 1, 4096, 32, 8, (8191,) * 8,
+                                        20240201),
+    # prefill of a second 4096-token chunk: attends to the previous chunk in
+    # the cache through the window and causally to itself (the pages' chunking)
+    "attn_prefill_bf16_T4096": AttnWorkload("attn_prefill_bf16_T4096", 1, 4096, 4096, 32, 8,
+                                            (4096,), 20240202),
+}
+
+
+def attn_inputs(w: AttnWorkload, device="cpu") -> dict:
+    """q [B,T,H,hd], k_new/v_new [B,T,KVH,hd], k_cache/v_cache [B,W,KVH,hd]
+    (bf16) and pos0 [B] (int32) of an attention workload."""
+    bf = torch.bfloat16
+    return dict(
+        q=_normal((w.B, w.T, w.H, w.hd), 1.0, device, _seed(w.seed, 0, "q"), bf),
+        k_new=_normal((w.B, w.T, w.KVH, w.hd), 1.0, device, _seed(w.seed, 0, "k_new"), bf),
+        v_new=_normal((w.B, w.T, w.KVH, w.hd), 1.0, device, _seed(w.seed, 0, "v_new"), bf),
+        k_cache=_normal((w.B, w.W, w.KVH, w.hd), 1.0, device, _seed(w.seed, 0, "k_cache"), bf),
+        v_cache=_normal((w.B, w.W, w.KVH, w.hd), 1.0, device, _seed(w.seed, 0, "v_cache"), bf),
+        pos0=torch.tensor(list(w.pos0), dtype=torch.int32, device=device),
+    )
