@@ -272,6 +272,76 @@ def run_workload(name, dev, steps, warmup):
     return res, layer
 
 
+def run_attention(dev, steps, warmup, cpu=True):
+    """The attention sub-block (sliding-window GQA with the rolling cache):
+    decode (8 sequences, one token each, full wrapped cache) and the prefill
+    of a 4096-token chunk after a previous chunk.  Each entry times
+    swa_attention (and the cache append) with HIP events, inputs resident."""
+    out = []
+    for name, w in W.ATTN_WORKLOADS.items():
+        inp = W.attn_inputs(w, dev)
+        ws = torch.empty(max(M.swa_workspace_size(w.B, w.T, w.W, w.H, w.KVH), 16),
+                         dtype=torch.uint8, device=dev)
+        o = torch.empty((w.B, w.T, w.H, w.hd), dtype=torch.bfloat16, device=dev)
+        kc, vc = inp["k_cache"].clone(), inp["v_cache"].clone()
+
+        def attn():
+            M.swa_attention(inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"],
+                            inp["v_cache"], inp["pos0"], w.W, out=o, workspace=ws)
+
+        def append():
+            M.swa_cache_append(inp["k_new"], inp["v_new"], inp["pos0"], kc, vc)
+
+        def timed(fn):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / steps
+
+        ms = timed(attn)
+        ms_append = timed(append)
+        # keys each query attends to: the window, capped by the positions that exist
+        keys = sum(min(w.W, p + t + 1) for p in w.pos0 for t in range(w.T))
+        flops = 4.0 * keys * w.H * w.hd                      # q.k and p.v, 2 flops per MAC
+        cache_rows = sum(min(w.W - 1, p) for p in w.pos0)    # cache positions read
+        kv_bytes = 2 * 2 * w.KVH * w.hd * (cache_rows + w.B * w.T)
+        io_bytes = 2 * w.B * w.T * w.H * w.hd * 2            # q read, out written
+        alg_bytes = kv_bytes + io_bytes
+        t_roof = max(alg_bytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+        bound = "hbm" if alg_bytes / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) \
+            else "mfma"
+        res = dict(workload=name, B=w.B, T=w.T, W=w.W, heads=w.H, kv_heads=w.KVH,
+                   pos0=list(w.pos0), ms_per_call=round(ms, 4),
+                   tokens_per_s=round(w.B * w.T / (ms * 1e-3), 1),
+                   ms_cache_append=round(ms_append, 4), bound=bound,
+                   algorithmic_bytes=int(alg_bytes), algorithmic_flops=flops,
+                   achieved=round(alg_bytes / (ms * 1e-3) / 1e9, 1) if bound == "hbm"
+                   else round(flops / (ms * 1e-3) / 1e12, 1),
+                   unit="GB/s" if bound == "hbm" else "TFLOP/s",
+                   roofline_frac=round(t_roof / (ms * 1e-3), 4),
+                   key_splits=M.swa_workspace_size(w.B, w.T, w.W, w.H, w.KVH) > 0)
+        if cpu and w.T == 1:
+            from oracle import swa_oracle as A
+            t0 = time.perf_counter()
+            npi = {k: v.detach().double().cpu().numpy() for k, v in inp.items() if k != "pos0"}
+            t0 = time.perf_counter()
+            for b in range(w.B):
+                A.swa_chunk_attention(npi["q"][b], npi["k_new"][b], npi["v_new"][b],
+                                      npi["k_cache"][b], npi["v_cache"][b], w.pos0[b], w.W)
+            res["oracle_s"] = round(time.perf_counter() - t0, 3)
+        out.append(res)
+        del inp, ws, o, kc, vc
+        torch.cuda.empty_cache()
+    return out
+
+
 def run_decode_sweep(dev, steps, warmup):
     """Small batches through the decode-shape layer (T = 1 .. 64)."""
     out = []
@@ -395,6 +465,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps(dict(copy_bytes_read=n, copy_bytes_written=n, calls=args.steps)))
         return
+    if args.only == "attention":
+        print(json.dumps(run_attention(dev, args.steps, args.warmup, cpu=False)), flush=True)
+        return
     if args.only:
         res, _ = run_workload(args.only, dev, args.steps, args.warmup)
         print(json.dumps(res), flush=True)
@@ -416,6 +489,11 @@ def main():
             del lay
             torch.cuda.empty_cache()
     decode_sweep = [] if args.no_sweep else run_decode_sweep(dev, max(5, args.steps // 5), 2)
+    attention = [] if args.no_sweep else run_attention(dev, max(10, args.steps // 2), 3,
+                                                       cpu=not args.no_cpu)
+    for r in attention:
+        print("# %s done: %.4f ms/call" % (r["workload"], r["ms_per_call"]), file=sys.stderr,
+              flush=True)
     stack = None if (args.no_sweep or args.no_stack) else run_stacks(dev, 3, 1, 10)
     for r in stack or []:
         print("# %s done: %.1f ms/step" % (r["workload"], r["ms_per_step"]), file=sys.stderr,
@@ -442,6 +520,7 @@ def main():
         "sweep": sweep,
         "decode_sweep": decode_sweep,
         "stack": stack,
+        "attention": attention,
     }
     print(json.dumps(out), flush=True)
 
