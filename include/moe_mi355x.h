@@ -245,7 +245,7 @@ moe_status swa_workspace_size(int64_t B, int64_t T, int64_t W, int32_t n_heads,
 /* One chunk of sliding-window grouped-query attention (sections 1.1, 1.2.1,
  * 1.2.3).  workspace: device buffer of swa_workspace_size bytes, 256-byte
  * aligned (may be NULL when that is 0).  All pointers 16-byte aligned; out
- * may not overlap q, k_new, v_new or the cache. */
+ * may not overlap q, k_new, v_new or the cache.  pos0[b] >= 0. */
 moe_status swa_attention(const void* q, const void* k_new, const void* v_new,
                          const void* k_cache, const void* v_cache, const int32_t* pos0,
                          int64_t B, int64_t T, int64_t W, int32_t n_heads, int32_t n_kv_heads,

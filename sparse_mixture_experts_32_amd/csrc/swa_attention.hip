@@ -15,20 +15,25 @@
 //     head w % G and kQSub tiles of 16 tokens, so every key/value tile
 //     staged in LDS serves all heads of the group;
 //   * keys go in blocks of 64: K and V rows (256 bytes each) travel global ->
-//     LDS with global_load_lds_dwordx4, double buffered; each row's 16-byte
-//     chunks are XOR-swizzled so the operand reads are free of bank
-//     conflicts;
+//     LDS with global_load_lds_dwordx4 through a ring of 2 or 4 slots; each
+//     row's 16-byte chunks are XOR-swizzled so the operand reads are free of
+//     bank conflicts; workgroups of one key/value head are placed on one XCD
+//     so their overlapping windows share an L2;
 //   * scores: S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (keys on the M side,
-//     queries on the N side), so a lane holds 8 keys of one query;
-//   * online softmax per query (running max and sum, exp2 with the scale
-//     folded in); the probabilities are rounded to bf16 and are, as held,
-//     the N-side operand of O^T = V^T P^T -- the matrix instruction's k
-//     order is taken to be the lane's key order, and the V^T operand is read
-//     in that same order with ds_read_b64_tr_b16 (4 keys of one column per
-//     read);
+//     queries on the N side), so a lane holds 8 keys of one query; scores
+//     are masked only in blocks at the window's edges;
+//   * online softmax per query with a lazily moved reference (exp2 with the
+//     scale folded in; the O rescale happens only when the maximum grows by
+//     more than 2^8); the probabilities are rounded to bf16 and are, as
+//     held, the N-side operand of O^T = V^T P^T -- the matrix instruction's
+//     k order is taken to be the lane's key order, and the V^T operand is
+//     read in that same order with ds_read_b64_tr_b16 (4 keys of one column
+//     per read); a ones operand against the same weights gives the sums;
 //   * long windows with few query tiles (decode) split the key range over
-//     workgroups; each writes its unnormalised output, running max and sum,
+//     workgroups; each writes its unnormalised output, reference and sum,
 //     and a combine kernel merges the splits in split order.
+#include <type_traits>
+
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -74,12 +79,49 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
 __device__ __forceinline__ int swz_k(int r) { return r & 15; }
 __device__ __forceinline__ int swz_v(int r) { return 2 * (r & 3) + 8 * ((r >> 2) & 1); }
 
-template <int kQSub>
-__global__ __launch_bounds__(256, 2) void swa_attn_kernel(AttnArgs a) {
-  __shared__ __align__(1024) char sK0[kTile], sK1[kTile], sV0[kTile], sV1[kTile];
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Max over the four 16-lane rows that hold the same query column: the
+// permlane swaps exchange rows 0<->1, 2<->3 (16) and the halves (32); of the
+// two results one is the lane's own value and one its partner's.
+__device__ __forceinline__ float max_rows(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// two floats -> two bf16 (round to nearest even, the hardware conversion)
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int S>
+using slot_c = std::integral_constant<int, S>;
+
+// kQSub: 16-token query tiles per wave.  kSlots: key/value blocks in the LDS
+// ring (kSlots - 1 in flight while one is consumed).  kOcc: workgroups per
+// CU -- with two, each wave has 256 registers, with one 512.
+template <int kQSub, int kSlots, int kOcc>
+__global__ __launch_bounds__(256, kOcc) void swa_attn_kernel(AttnArgs a) {
+  static_assert(kOcc == 1 || kSlots == 2, "two workgroups per CU fit two 32 KB slots each");
+  static_assert(kSlots == 2 || kSlots == 4, "ring of 2 or 4 slots");
+  __shared__ __align__(1024) char sK0[kTile], sV0[kTile], sK1[kTile], sV1[kTile];
+  __shared__ __align__(1024) char sK2[kSlots > 2 ? kTile : 1], sV2[kSlots > 2 ? kTile : 1];
+  __shared__ __align__(1024) char sK3[kSlots > 2 ? kTile : 1], sV3[kSlots > 2 ? kTile : 1];
 
   // ---- which (sequence, kv head, query tile, key split) ----
+  // Work items are numbered split-fastest; consecutive items go to the same
+  // XCD (the hardware deals workgroups round-robin over the 8 XCDs), so the
+  // query tiles of one kv head, whose key windows overlap, share an L2.
   int bid = blockIdx.x;
+  if ((gridDim.x & 7) == 0) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
   const int split = bid % a.splits;
   bid /= a.splits;
   const int qt = bid % a.qtiles;
@@ -108,6 +150,9 @@ __global__ __launch_bounds__(256, 2) void swa_attn_kernel(AttnArgs a) {
   const int nblk = max(0, min(nblk_all, blk0 + per) - blk0);
   const int k_lo = k_first + blk0 * kKB;                          // this split's keys
   const int k_hi = min(k_last, k_lo + nblk * kKB - 1);
+  // positions of this wave's first and last (clamped) query rows
+  const int wq_lo = pos0 + min(t_base, T - 1);
+  const int wq_hi = pos0 + min(t_base + 16 * kQSub - 1, T - 1);
 
   const int g = lane >> 4;
   const int j = lane & 15;
@@ -126,37 +171,77 @@ __global__ __launch_bounds__(256, 2) void swa_attn_kernel(AttnArgs a) {
   }
 
   // ---- key/value tile loads: 32 instructions per block, 8 per wave ----
-  // instruction i fills rows 4 (i mod 16) .. +3 of the K tile (i < 16) or V
-  // tile; lane l lands chunk l mod 16 of row 4 (i mod 16) + l / 16
-  auto issue = [&](int blk, char* kdst, char* vdst) {
-    const int kb = k_lo + blk * kKB;
+  // instruction u of wave w fills rows 32 (w mod 2) + 4 u .. +3 of the K
+  // tile (waves 0, 1) or the V tile (waves 2, 3); lane l lands chunk l mod 16
+  // of row 32 (w mod 2) + 4 u + l / 16.  A key at position kp < pos0 lies
+  // within one window before pos0, so its cache slot is
+  // kp - pos0 + (pos0 mod W), plus W when that is negative; a key at
+  // kp >= pos0 is chunk row kp - pos0.
+  const bool wave_v = wave >= 2;
+  const int row_bytes = a.KVH * kRowBytes;                        // bytes per position
+  const char* cache_base = reinterpret_cast<const char*>(wave_v ? a.v_cache : a.k_cache) +
+                           (int64_t)b * W * row_bytes + kv * kRowBytes;
+  const char* chunk_base = reinterpret_cast<const char*>(wave_v ? a.v_new : a.k_new) +
+                           (int64_t)b * T * row_bytes + kv * kRowBytes;
+  const int pos0_slot = pos0 % W;
+  const int row_w = 32 * (wave & 1) + (lane >> 4);                // + 4 u
+  uint32_t lane_off[8];                                           // within a block: row, chunk
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = wave * 8 + u;
-      const bool isv = i >= 16;
-      const int row = 4 * (i & 15) + (lane >> 4);
-      const int c = (lane & 15) ^ (isv ? swz_v(row) : swz_k(row));
-      const int kp = min(kb + row, k_hi);                  // rows past the range: masked
-      // both candidate rows, then a select: no divergent branch around the load
-      const bf16_t* from_cache = (isv ? a.v_cache : a.k_cache) +
-                                 ((int64_t)b * W + kp % W) * kv_stride;
-      const bf16_t* from_chunk = (isv ? a.v_new : a.k_new) +
-                                 ((int64_t)b * T + max(kp - pos0, 0)) * kv_stride;
-      const bf16_t* row_src = kp < pos0 ? from_cache : from_chunk;
-      dma16(row_src + (int64_t)kv * kHd + 8 * c, (isv ? vdst : kdst) + (i & 15) * 1024);
+  for (int u = 0; u < 8; ++u) {
+    const int row = row_w + 4 * u;
+    const int c = (lane & 15) ^ (wave_v ? swz_v(row) : swz_k(row));
+    lane_off[u] = (uint32_t)(row * row_bytes + 16 * c);
+  }
+  auto issue = [&](int blk, char* kdst, char* vdst) __attribute__((always_inline)) {
+    const int kb = k_lo + blk * kKB;
+    char* dst = wave_v ? vdst : kdst;
+    const int e0 = kb - pos0;                          // first key relative to pos0
+    const int slot0 = e0 + pos0_slot + (e0 + pos0_slot < 0 ? W : 0);
+    const bool whole = kb + kKB - 1 <= k_hi;
+    if (whole && (e0 >= 0 || (e0 + kKB <= 0 && slot0 + kKB <= W))) {
+      // all 64 rows from one source, consecutive: a uniform base + fixed offsets
+      const char* base = e0 >= 0 ? chunk_base + (int64_t)e0 * row_bytes
+                                 : cache_base + (int64_t)slot0 * row_bytes;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        dma16(base + lane_off[u], dst + (8 * (wave & 1) + u) * 1024);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int row = row_w + 4 * u;
+        const int c = (lane & 15) ^ (wave_v ? swz_v(row) : swz_k(row));
+        const int e = min(kb + row, k_hi) - pos0;        // rows past the range: masked
+        const int slot = e + pos0_slot + (e + pos0_slot < 0 ? W : 0);
+        const bool cached = e < 0;
+        const char* src = (cached ? cache_base : chunk_base) +
+                          (int64_t)(cached ? slot : e) * row_bytes + 16 * c;
+        dma16(src, dst + (8 * (wave & 1) + u) * 1024);
+      }
     }
   };
 
+  // Online softmax with a lazily moved reference: m is the exponent
+  // reference (log2 units, scale folded in); it moves only when a score
+  // exceeds it by more than kTau, so the weights 2^(s - m) stay below 2^kTau
+  // and the O rescale is rare.  The result O / l does not depend on m.
+  // The weight sums come from the matrix cores too (a ones operand against
+  // the same bf16 weights), so every entry of lsum[u] is the column's sum.
+  constexpr float kTau = 8.f;
   f32x4_t o[kQSub][8];
-  float m[kQSub], l[kQSub];
+  f32x4_t lsum[kQSub];
+  float m[kQSub];
 #pragma unroll
   for (int u = 0; u < kQSub; ++u) {
     m[u] = -1e30f;
-    l[u] = 0.f;
+    lsum[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < 8; ++db) o[u][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3f803f80u, 0x3f803f80u,
+                                                             0x3f803f80u, 0x3f803f80u});
   const float scale = kLog2e * 0.08838834764831845f;   // log2(e) / sqrt(128)
+  const float neg_inf = -__builtin_inff();
 
   // K operand (M side) of key row r, k-step s: chunk 4 s + g of row r
   int koff[2][4];
@@ -167,25 +252,22 @@ __global__ __launch_bounds__(256, 2) void swa_attn_kernel(AttnArgs a) {
       const int r = 16 * rb + j;
       koff[rb][s] = r * kRowBytes + (((4 * s + g) ^ swz_k(r)) << 4);
     }
-  // V^T operand: transposed read of rows k0 + i / 4, columns 16 db + 4 (i mod 4)
-  int voff[2][8];
+  // V^T operand: transposed read of rows k0 + i / 4, columns 16 db + 4 (i mod 4);
+  // the second 16 keys sit 16 rows (4 KB) further with the same swizzle
+  int voff[8];
 #pragma unroll
-  for (int half = 0; half < 2; ++half)
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const int r = 16 * half + 4 * g + (j >> 2);
-      const int col = 16 * db + 4 * (j & 3);
-      voff[half][db] = r * kRowBytes + (((col >> 3) ^ swz_v(r)) << 4) + (col & 7) * 2;
-    }
+  for (int db = 0; db < 8; ++db) {
+    const int r = 4 * g + (j >> 2);
+    const int col = 16 * db + 4 * (j & 3);
+    voff[db] = r * kRowBytes + (((col >> 3) ^ swz_v(r)) << 4) + (col & 7) * 2;
+  }
 
-  // one block of 64 keys from slot (kt, vt); the next block is loaded into
-  // the other slot meanwhile.  The loop below is unrolled over the two slots
-  // so the compiler sees which LDS object each read and each load touches.
-  auto stage = [&](int n, const char* kt, const char* vt, char* kn, char* vn) {
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0): block n has landed
-    __builtin_amdgcn_s_barrier();                      // ... for every wave; other slot free
-    if (n + 1 < nblk) issue(n + 1, kn, vn);
+  // 64 keys from one slot.  edge: the block holds keys that some query of
+  // this wave must not see (window edges, causal edge, end of the split's
+  // range); only then are scores masked.
+  auto compute = [&](int n, const char* kt, const char* vt) __attribute__((always_inline)) {
     const int kb = k_lo + n * kKB;
+    const bool edge = !(kb + kKB - 1 <= k_hi && kb + kKB - 1 <= wq_lo && kb > wq_hi - W);
 #pragma unroll
     for (int half32 = 0; half32 < 2; ++half32) {       // 32 keys at a time
       const char* kt32 = kt + half32 * 32 * kRowBytes;
@@ -200,15 +282,15 @@ __global__ __launch_bounds__(256, 2) void swa_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)((lds_char_t*)vt32 + voff[0][db]));
+            (lds_s16x4_t*)((lds_char_t*)vt32 + voff[db]));
         const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)((lds_char_t*)vt32 + voff[1][db]));
+            (lds_s16x4_t*)((lds_char_t*)vt32 + voff[db] + 16 * kRowBytes));
         const s16x4_t both[2] = {lo, hi};
         vf[db] = __builtin_bit_cast(bf16x8_t, both);
       }
 #pragma unroll
       for (int u = 0; u < kQSub; ++u) {
-        // scores of keys 16 rb + 4 g + i for query column j
+        // raw scores of keys 16 rb + 4 g + i for query column j
         f32x4_t sc[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
@@ -217,65 +299,104 @@ __global__ __launch_bounds__(256, 2) void swa_attn_kernel(AttnArgs a) {
           for (int s = 0; s < 4; ++s)
             sc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[rb][s], qf[u][s], sc[rb], 0, 0, 0);
         }
-        float sv[8];
-        bool ok[8];
-        float mx = -1e30f;
+        if (edge) {
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int kp = kb + half32 * 32 + 16 * rb + 4 * g + i;
+              const bool valid = kp <= k_hi && kp <= qpos[u] && kp > qpos[u] - W;
+              sc[rb][i] = valid ? sc[rb][i] : neg_inf;
+            }
+        }
+        float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        mx = max_rows(mx) * scale;
+        const bool move = mx > m[u] + kTau;
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {   // rare after the first block
+          const float m_new = move ? mx : m[u];
+          const float corr = __builtin_amdgcn_exp2f(m[u] - m_new);
+          m[u] = m_new;
+          lsum[u] *= corr;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) o[u][db] *= corr;
+        }
+        const float neg_m = -m[u];
+        float p[8];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int kp = kb + half32 * 32 + 16 * rb + 4 * g + i;
-            const bool valid = kp <= k_hi && kp <= qpos[u] && kp > qpos[u] - W;
-            const float v = sc[rb][i] * scale;
-            ok[4 * rb + i] = valid;
-            sv[4 * rb + i] = v;
-            if (valid) mx = fmaxf(mx, v);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m[u], mx);
-        const float corr = __builtin_amdgcn_exp2f(m[u] - m_new);
-        float ps = 0.f;
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = ok[e] ? __builtin_amdgcn_exp2f(sv[e] - m_new) : 0.f;
-          ps += p[e];
-        }
-        ps += __shfl_xor(ps, 16);
-        ps += __shfl_xor(ps, 32);
-        l[u] = l[u] * corr + ps;
-        m[u] = m_new;
-        uint4 pk;
-        pk.x = pack_bf16x2(p[0], p[1]);
-        pk.y = pack_bf16x2(p[2], p[3]);
-        pk.z = pack_bf16x2(p[4], p[5]);
-        pk.w = pack_bf16x2(p[6], p[7]);
+          for (int i = 0; i < 4; ++i)
+            p[4 * rb + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rb][i], scale, neg_m));
+        const u32x4_t pk = {cvt_bf16x2(p[0], p[1]), cvt_bf16x2(p[2], p[3]),
+                            cvt_bf16x2(p[4], p[5]), cvt_bf16x2(p[6], p[7])};
         const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pk);
 #pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          o[u][db] *= corr;
+        for (int db = 0; db < 8; ++db)
           o[u][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pf, o[u][db], 0, 0, 0);
-        }
+        lsum[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf, lsum[u], 0, 0, 0);
       }
     }
   };
 
+  auto slot_k = [&](auto s) __attribute__((always_inline)) -> char* {
+    constexpr int S = decltype(s)::value;
+    if constexpr (S == 0) return sK0;
+    else if constexpr (S == 1) return sK1;
+    else if constexpr (S == 2) return sK2;
+    else return sK3;
+  };
+  auto slot_v = [&](auto s) __attribute__((always_inline)) -> char* {
+    constexpr int S = decltype(s)::value;
+    if constexpr (S == 0) return sV0;
+    else if constexpr (S == 1) return sV1;
+    else if constexpr (S == 2) return sV2;
+    else return sV3;
+  };
+
+  // block n sits in slot S; block n + kSlots - 1 is loaded into the slot
+  // that block n - 1 used.  The ring is unrolled over its slots so that the
+  // compiler sees which LDS object each read and each load touches.
+  auto stage = [&](auto s, int n) __attribute__((always_inline)) {
+    constexpr int S = decltype(s)::value;
+    constexpr int SN = (S + kSlots - 1) % kSlots;
+    if constexpr (kSlots == 2) {
+      wait_vm<0>();                                      // block n has landed
+    } else {
+      const int ahead = min(kSlots - 2, nblk - 1 - n);   // blocks issued after n
+      if (ahead >= 2) wait_vm<16>();
+      else if (ahead == 1) wait_vm<8>();
+      else wait_vm<0>();
+    }
+    __builtin_amdgcn_s_barrier();      // ... for every wave; slot SN is free
+    if (n + kSlots - 1 < nblk) issue(n + kSlots - 1, slot_k(slot_c<SN>{}), slot_v(slot_c<SN>{}));
+    compute(n, slot_k(s), slot_v(s));
+  };
+
   if (nblk > 0) issue(0, sK0, sV0);
-  for (int n = 0; n < nblk; n += 2) {
-    stage(n, sK0, sV0, sK1, sV1);
-    if (n + 1 < nblk) stage(n + 1, sK1, sV1, sK0, sV0);
+  if constexpr (kSlots == 4) {
+    if (nblk > 1) issue(1, sK1, sV1);
+    if (nblk > 2) issue(2, sK2, sV2);
   }
-  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));     // no load lands after the end
+  for (int n = 0; n < nblk; n += kSlots) {
+    stage(slot_c<0>{}, n);
+    if (n + 1 < nblk) stage(slot_c<1>{}, n + 1);
+    if constexpr (kSlots == 4) {
+      if (n + 2 < nblk) stage(slot_c<2>{}, n + 2);
+      if (n + 3 < nblk) stage(slot_c<3>{}, n + 3);
+    }
+  }
+  wait_vm<0>();                                          // no load lands after the end
 
   // ---- output: lane holds d = 16 db + 4 g .. +3 of query token t ----
 #pragma unroll
   for (int u = 0; u < kQSub; ++u) {
+    const float l = lsum[u][0];
     const int t = t_base + 16 * u + j;
     if (t >= T) continue;
     const int64_t row = ((int64_t)b * T + t) * a.H + h;
     if (a.splits == 1) {
-      const float inv = l[u] > 0.f ? 1.f / l[u] : 0.f;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         const int d = 16 * db + 4 * g;
@@ -300,14 +421,15 @@ __global__ __launch_bounds__(256, 2) void swa_attn_kernel(AttnArgs a) {
       }
       if (g == 0) {
         a.part_ml[prow * 2 + 0] = m[u];
-        a.part_ml[prow * 2 + 1] = l[u];
+        a.part_ml[prow * 2 + 1] = l;
       }
     }
   }
 }
 
 // Merge the key splits of each (sequence, token, head) in split order:
-// o = sum_s 2^(m_s - m) o_s / sum_s 2^(m_s - m) l_s with m = max_s m_s.
+// o = sum_s 2^(m_s - m) o_s / sum_s 2^(m_s - m) l_s with m = max_s m_s.  A
+// split that saw no key of the row has l_s = 0 and o_s = 0 and weighs 0.
 __global__ __launch_bounds__(128) void swa_combine_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
                                                           int rows, int splits, void* out,
@@ -316,16 +438,19 @@ __global__ __launch_bounds__(128) void swa_combine_kernel(const float* __restric
   const int d = threadIdx.x;
   if (row >= rows) return;
   const float* ml = part_ml + (int64_t)row * splits * 2;
+  const float* po = part_o + (int64_t)row * splits * kHd + d;
   float mmax = -1e30f;
-  for (int s = 0; s < splits; ++s)
-    if (ml[2 * s + 1] > 0.f) mmax = fmaxf(mmax, ml[2 * s]);
-  float num = 0.f, den = 0.f;
   for (int s = 0; s < splits; ++s) {
-    const float ls = ml[2 * s + 1];
-    if (ls <= 0.f) continue;
-    const float w = __builtin_amdgcn_exp2f(ml[2 * s] - mmax);
-    num += w * part_o[((int64_t)row * splits + s) * kHd + d];
-    den += w * ls;
+    const float ms = ml[2 * s], ls = ml[2 * s + 1];
+    mmax = ls > 0.f ? fmaxf(mmax, ms) : mmax;
+  }
+  float num = 0.f, den = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < splits; ++s) {
+    const float ms = ml[2 * s], ls = ml[2 * s + 1];
+    const float w = ls > 0.f ? __builtin_amdgcn_exp2f(ms - mmax) : 0.f;
+    num = __builtin_fmaf(w, po[(int64_t)s * kHd], num);
+    den = __builtin_fmaf(w, ls, den);
   }
   const float v = den > 0.f ? num / den : 0.f;
   if (out_f32)
@@ -364,18 +489,30 @@ __global__ __launch_bounds__(256) void swa_append_kernel(const bf16_t* __restric
 
 int swa_head_dim() { return kHd; }
 
-// Key splits: enough workgroups to cover the chip when the query tiles alone
-// do not (decode), each split at least 4 blocks of keys.
+// Launch plan.  Chunks of 64 tokens or more: two 16-token tiles per wave
+// (each K/V fragment read from LDS serves 32 query columns), a 2-slot ring
+// and two workgroups per CU, so that each SIMD runs two waves and the matrix
+// work of one overlaps the softmax of the other.  (Four tiles per wave need
+// more than the 256 registers a wave has at that occupancy; at one
+// workgroup per CU they measured slower.)  Shorter chunks (decode): one tile
+// per wave and a 4-slot ring, one workgroup per CU, three blocks of keys in
+// flight.  Key splits are added until the chip is covered (512 resident
+// workgroups, resp. 256), each split at least 4 blocks of 64 keys.
+constexpr int kBigQSub = 2;          // query tiles per wave for chunks of 64 tokens or more
+constexpr int kBigOcc = kBigQSub == 2 ? 2 : 1;
+
 int swa_plan_splits(int B, int T, int W, int H, int KVH, int* qtiles_out, int* qsub_out) {
   const int G = H / KVH;
-  const int qsub = T >= 64 ? 2 : 1;
+  const bool big = T >= 64;
+  const int qsub = big ? kBigQSub : 1;
   const int wg_tokens = 16 * qsub * (kWaves / G);
   const int qtiles = (T + wg_tokens - 1) / wg_tokens;
   const int64_t wgs = (int64_t)B * KVH * qtiles;
+  const int64_t target = big ? 256 * kBigOcc : 256;
   const int keys = min(W, T) + W;                  // generous upper bound of a tile's range
   const int max_splits = max(1, keys / (4 * kKB));
   int splits = 1;
-  while (splits < max_splits && wgs * splits < 1024) splits *= 2;
+  while (splits < max_splits && wgs * splits < target) splits *= 2;
   splits = min(splits, max_splits);
   if (qtiles_out) *qtiles_out = qtiles;
   if (qsub_out) *qsub_out = qsub;
@@ -409,10 +546,11 @@ hipError_t launch_swa_attention(const void* q, const void* k_new, const void* v_
   a.out_f32 = out_f32;
   const int64_t grid = (int64_t)B * KVH * qtiles * splits;
   if (grid == 0) return hipSuccess;
-  if (qsub == 2)
-    hipLaunchKernelGGL(swa_attn_kernel<2>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  if (qsub == 1)
+    hipLaunchKernelGGL((swa_attn_kernel<1, 4, 1>), dim3((unsigned)grid), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(swa_attn_kernel<1>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((swa_attn_kernel<kBigQSub, 2, kBigOcc>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   const int rows = B * T * H;
