@@ -272,6 +272,32 @@ def run_workload(name, dev, steps, warmup):
     return res, layer
 
 
+# the attention kernel each workload runs: chunks of 64 tokens or more take
+# two 16-token tiles per wave and a 2-slot ring, shorter ones one tile and 4 slots
+ATTN_KERNEL = {True: "swa_attn_kernel<2, 2, 2>", False: "swa_attn_kernel<1, 4, 1>"}
+ATTN_COUNTERS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                             "attn_counters.txt")
+
+
+def attn_traffic(kernel, workload):
+    """Calibrated FETCH+WRITE bytes per dispatch of the attention kernel, or
+    None when no row matches or swa_attention.hip changed since the counters
+    were taken."""
+    try:
+        import hashlib
+        sha = hashlib.sha256(open(os.path.join(CSRC, "swa_attention.hip"), "rb").read()).hexdigest()
+        text = open(ATTN_COUNTERS).read()
+    except OSError:
+        return None
+    if ("swa_attention.hip: " + sha) not in text:
+        return None
+    for ln in text.splitlines():
+        r = [c.strip() for c in ln.split("|")]
+        if not ln.startswith("#") and len(r) >= 6 and r[0] == kernel and r[1] == workload:
+            return int(r[5])
+    return None
+
+
 def run_attention(dev, steps, warmup, cpu=True):
     """The attention sub-block (sliding-window GQA with the rolling cache):
     decode (8 sequences, one token each, full wrapped cache) and the prefill
@@ -317,16 +343,23 @@ def run_attention(dev, steps, warmup, cpu=True):
         t_roof = max(alg_bytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
         bound = "hbm" if alg_bytes / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) \
             else "mfma"
+        achieved = (alg_bytes / (ms * 1e-3) / 1e9 if bound == "hbm"
+                    else flops / (ms * 1e-3) / 1e12)
+        peak = HBM_PEAK_GBS if bound == "hbm" else MFMA_BF16_PEAK_TFLOPS
+        kernel = ATTN_KERNEL[w.T >= 64]
         res = dict(workload=name, B=w.B, T=w.T, W=w.W, heads=w.H, kv_heads=w.KVH,
                    pos0=list(w.pos0), ms_per_call=round(ms, 4),
                    tokens_per_s=round(w.B * w.T / (ms * 1e-3), 1),
                    ms_cache_append=round(ms_append, 4), bound=bound,
                    algorithmic_bytes=int(alg_bytes), algorithmic_flops=flops,
-                   achieved=round(alg_bytes / (ms * 1e-3) / 1e9, 1) if bound == "hbm"
-                   else round(flops / (ms * 1e-3) / 1e12, 1),
+                   achieved=round(achieved, 1),
                    unit="GB/s" if bound == "hbm" else "TFLOP/s",
                    roofline_frac=round(t_roof / (ms * 1e-3), 4),
-                   key_splits=M.swa_workspace_size(w.B, w.T, w.W, w.H, w.KVH) > 0)
+                   key_splits=M.swa_workspace_size(w.B, w.T, w.W, w.H, w.KVH) > 0,
+                   roofline=dict(kernel=kernel, bound=bound, achieved=round(achieved, 1),
+                                 peak=peak, unit="GB/s" if bound == "hbm" else "TFLOP/s",
+                                 frac=round(achieved / peak, 4),
+                                 traffic=attn_traffic(kernel, name)))
         if cpu and w.T == 1:
             from oracle import swa_oracle as A
             t0 = time.perf_counter()

@@ -262,43 +262,61 @@ __global__ __launch_bounds__(256, kOcc) void swa_attn_kernel(AttnArgs a) {
     voff[db] = r * kRowBytes + (((col >> 3) ^ swz_v(r)) << 4) + (col & 7) * 2;
   }
 
-  // 64 keys from one slot.  edge: the block holds keys that some query of
-  // this wave must not see (window edges, causal edge, end of the split's
-  // range); only then are scores masked.
+  // Operand reads of 32 keys: K rows as the M-side operand of the scores,
+  // V^T (transposed reads) as the M-side operand of O^T.
+  auto read_k = [&](const char* kt32, bf16x8_t (&kf)[2][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        kf[rb][s] = *reinterpret_cast<const bf16x8_t*>(kt32 + koff[rb][s]);
+  };
+  auto read_v = [&](const char* vt32, bf16x8_t (&vf)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)((lds_char_t*)vt32 + voff[db]));
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)((lds_char_t*)vt32 + voff[db] + 16 * kRowBytes));
+      const s16x4_t both[2] = {lo, hi};
+      vf[db] = __builtin_bit_cast(bf16x8_t, both);
+    }
+  };
+
+  // 64 keys from one slot, as two halves of 32.  The reads of the second
+  // half are issued behind the first half's score products (K) and behind
+  // its P.V products (V), into the registers those products have consumed,
+  // so their latency hides under the softmax and the matrix work.  edge:
+  // the block holds keys that some query of this wave must not see (window
+  // edges, causal edge, end of the split's range); only then are scores
+  // masked.
   auto compute = [&](int n, const char* kt, const char* vt) __attribute__((always_inline)) {
     const int kb = k_lo + n * kKB;
     const bool edge = !(kb + kKB - 1 <= k_hi && kb + kKB - 1 <= wq_lo && kb > wq_hi - W);
+    bf16x8_t kf[2][4];
+    bf16x8_t vf[8];
+    read_k(kt, kf);
+    read_v(vt, vf);
 #pragma unroll
     for (int half32 = 0; half32 < 2; ++half32) {       // 32 keys at a time
-      const char* kt32 = kt + half32 * 32 * kRowBytes;
-      const char* vt32 = vt + half32 * 32 * kRowBytes;
-      bf16x8_t kf[2][4];
+      // raw scores of keys 16 rb + 4 g + i for query column j, all tiles
+      f32x4_t sc[kQSub][2];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int u = 0; u < kQSub; ++u)
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          kf[rb][s] = *reinterpret_cast<const bf16x8_t*>(kt32 + koff[rb][s]);
-      bf16x8_t vf[8];
+        for (int rb = 0; rb < 2; ++rb) {
+          sc[u][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)((lds_char_t*)vt32 + voff[db]));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)((lds_char_t*)vt32 + voff[db] + 16 * kRowBytes));
-        const s16x4_t both[2] = {lo, hi};
-        vf[db] = __builtin_bit_cast(bf16x8_t, both);
+          for (int s = 0; s < 4; ++s)
+            sc[u][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[rb][s], qf[u][s], sc[u][rb], 0, 0, 0);
+        }
+      if (half32 == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        read_k(kt + 32 * kRowBytes, kf);
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int u = 0; u < kQSub; ++u) {
-        // raw scores of keys 16 rb + 4 g + i for query column j
-        f32x4_t sc[2];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          sc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            sc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[rb][s], qf[u][s], sc[rb], 0, 0, 0);
-        }
         if (edge) {
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
@@ -306,11 +324,11 @@ __global__ __launch_bounds__(256, kOcc) void swa_attn_kernel(AttnArgs a) {
             for (int i = 0; i < 4; ++i) {
               const int kp = kb + half32 * 32 + 16 * rb + 4 * g + i;
               const bool valid = kp <= k_hi && kp <= qpos[u] && kp > qpos[u] - W;
-              sc[rb][i] = valid ? sc[rb][i] : neg_inf;
+              sc[u][rb][i] = valid ? sc[u][rb][i] : neg_inf;
             }
         }
-        float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        float mx = fmaxf(fmaxf(fmaxf(sc[u][0][0], sc[u][0][1]), fmaxf(sc[u][0][2], sc[u][0][3])),
+                         fmaxf(fmaxf(sc[u][1][0], sc[u][1][1]), fmaxf(sc[u][1][2], sc[u][1][3])));
         mx = max_rows(mx) * scale;
         const bool move = mx > m[u] + kTau;
         if (__builtin_amdgcn_ballot_w64(move) != 0) {   // rare after the first block
@@ -327,7 +345,7 @@ __global__ __launch_bounds__(256, kOcc) void swa_attn_kernel(AttnArgs a) {
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            p[4 * rb + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rb][i], scale, neg_m));
+            p[4 * rb + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][rb][i], scale, neg_m));
         const u32x4_t pk = {cvt_bf16x2(p[0], p[1]), cvt_bf16x2(p[2], p[3]),
                             cvt_bf16x2(p[4], p[5]), cvt_bf16x2(p[6], p[7])};
         const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pk);
@@ -335,6 +353,11 @@ __global__ __launch_bounds__(256, kOcc) void swa_attn_kernel(AttnArgs a) {
         for (int db = 0; db < 8; ++db)
           o[u][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pf, o[u][db], 0, 0, 0);
         lsum[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf, lsum[u], 0, 0, 0);
+      }
+      if (half32 == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        read_v(vt + 32 * kRowBytes, vf);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
