@@ -126,29 +126,35 @@ def algorithmic(w: W.Workload, counts):
 
 
 def time_layer(layer: Layer, steps: int, warmup: int):
+    """The timed step is one moe_forward call (all kernels of the layer on the
+    current stream, no host synchronisation inside): `steps` of them between
+    two synchronisations.  A second pass runs the same kernels through the
+    stage entry points with HIP events between them, for per-kernel times.
+    Returns (wall seconds of the moe_forward steps, per-stage mean ms, wall
+    seconds of the staged steps)."""
     for _ in range(warmup):
+        layer.forward_call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.forward_call()
+    torch.cuda.synchronize()
+    wall_fwd = time.perf_counter() - t0
+    # staged pass: the same kernels, HIP events between the stages
+    for _ in range(max(1, warmup // 2)):
         layer.step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
            for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    t1 = time.perf_counter()
     for i in range(steps):
         layer.step(evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_staged = time.perf_counter() - t1
     per_stage = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
                  for j, name in enumerate(STAGES)}
-    # the single-call path, for reference
-    for _ in range(max(1, warmup // 2)):
-        layer.forward_call()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for _ in range(steps):
-        layer.forward_call()
-    torch.cuda.synchronize()
-    wall_fwd = time.perf_counter() - t1
-    return wall, per_stage, wall_fwd
+    return wall_fwd, per_stage, wall_staged
 
 
 FLUSH_BYTES = 1 << 30
@@ -157,21 +163,33 @@ FLUSH_BYTES = 1 << 30
 def time_cold(layer: Layer, steps: int):
     """Each step timed alone with HIP events after writing a 1 GiB buffer, so
     neither L2 nor the 256 MB Infinity Cache holds a tail of the weights from
-    the previous step.  Returns per-stage means and step percentiles (ms)."""
+    the previous step: moe_forward steps (percentiles of the whole call), then
+    staged steps (per-stage means, for the kernel roofline)."""
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=layer.x.device)
-    per = []
+    tot = []
     for i in range(steps):
         flush.fill_(i & 0xFF)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        layer.forward_call()
+        e1.record()
+        torch.cuda.synchronize()
+        tot.append(e0.elapsed_time(e1))
+    per = []
+    for i in range(steps):
+        flush.fill_((i + 7) & 0xFF)
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
         layer.step(evs)
         torch.cuda.synchronize()
         per.append([evs[j].elapsed_time(evs[j + 1]) for j in range(len(STAGES))])
     del flush
     per = np.asarray(per)
-    tot = per.sum(axis=1)
+    tot = np.asarray(tot)
     return dict(steps=steps, ms_median=round(float(np.median(tot)), 4),
                 ms_p10=round(float(np.percentile(tot, 10)), 4),
                 ms_p90=round(float(np.percentile(tot, 90)), 4),
+                staged_ms_median=round(float(np.median(per.sum(axis=1))), 4),
                 stage_ms={name: round(float(per[:, j].mean()), 4) for j, name in enumerate(STAGES)})
 
 
@@ -253,12 +271,12 @@ def run_workload(name, dev, steps, warmup):
     layer.step()
     torch.cuda.synchronize()
     counts = layer.counts()
-    wall, per_stage, wall_fwd = time_layer(layer, steps, warmup)
+    wall, per_stage, wall_staged = time_layer(layer, steps, warmup)
     alg = algorithmic(w, counts)
     ms = wall / steps * 1e3
     res = dict(workload=name, T=w.T, steps=steps, ms_per_step=round(ms, 4),
                tokens_per_s=round(w.T * steps / wall, 1),
-               ms_per_step_single_call=round(wall_fwd / steps * 1e3, 4),
+               ms_per_step_staged=round(wall_staged / steps * 1e3, 4),
                stage_ms={k: round(v, 4) for k, v in per_stage.items()},
                n_active_experts=alg["n_active"], expert_counts=counts.tolist(),
                plan=layer.plan, routing=layer.routing_stats(),
