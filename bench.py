@@ -291,8 +291,8 @@ def run_workload(name, dev, steps, warmup):
 
 
 # the attention kernel each workload runs: chunks of 64 tokens or more take
-# two 16-token tiles per wave and a 2-slot ring, shorter ones one tile and 4 slots
-ATTN_KERNEL = {True: "swa_attn_kernel<2, 2, 2>", False: "swa_attn_kernel<1, 4, 1>"}
+# two 16-token tiles per wave, shorter ones one tile
+ATTN_KERNEL = {True: "swa_attn_kernel<2>", False: "swa_attn_kernel<1>"}
 ATTN_COUNTERS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                              "attn_counters.txt")
 

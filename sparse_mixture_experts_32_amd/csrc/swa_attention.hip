@@ -15,7 +15,7 @@
 //     head w % G and kQSub tiles of 16 tokens, so every key/value tile
 //     staged in LDS serves all heads of the group;
 //   * keys go in blocks of 64: K and V rows (256 bytes each) travel global ->
-//     LDS with global_load_lds_dwordx4 through a ring of 2 or 4 slots; each
+//     LDS with global_load_lds_dwordx4, double buffered; each
 //     row's 16-byte chunks are XOR-swizzled so the operand reads are free of
 //     bank conflicts; workgroups of one key/value head are placed on one XCD
 //     so their overlapping windows share an L2;
@@ -32,8 +32,6 @@
 //   * long windows with few query tiles (decode) split the key range over
 //     workgroups; each writes its unnormalised output, reference and sum,
 //     and a combine kernel merges the splits in split order.
-#include <type_traits>
-
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -102,19 +100,12 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int S>
-using slot_c = std::integral_constant<int, S>;
-
-// kQSub: 16-token query tiles per wave.  kSlots: key/value blocks in the LDS
-// ring (kSlots - 1 in flight while one is consumed).  kOcc: workgroups per
-// CU -- with two, each wave has 256 registers, with one 512.
-template <int kQSub, int kSlots, int kOcc>
-__global__ __launch_bounds__(256, kOcc) void swa_attn_kernel(AttnArgs a) {
-  static_assert(kOcc == 1 || kSlots == 2, "two workgroups per CU fit two 32 KB slots each");
-  static_assert(kSlots == 2 || kSlots == 4, "ring of 2 or 4 slots");
+// kQSub: 16-token query tiles per wave.  Two workgroups per CU (each wave
+// has 256 registers), each with a 2-slot ring: one block of keys in flight
+// while the other is consumed.
+template <int kQSub>
+__global__ __launch_bounds__(256, 2) void swa_attn_kernel(AttnArgs a) {
   __shared__ __align__(1024) char sK0[kTile], sV0[kTile], sK1[kTile], sV1[kTile];
-  __shared__ __align__(1024) char sK2[kSlots > 2 ? kTile : 1], sV2[kSlots > 2 ? kTile : 1];
-  __shared__ __align__(1024) char sK3[kSlots > 2 ? kTile : 1], sV3[kSlots > 2 ? kTile : 1];
 
   // ---- which (sequence, kv head, query tile, key split) ----
   // Work items are numbered split-fastest; consecutive items go to the same
@@ -362,52 +353,21 @@ __global__ __launch_bounds__(256, kOcc) void swa_attn_kernel(AttnArgs a) {
     }
   };
 
-  auto slot_k = [&](auto s) __attribute__((always_inline)) -> char* {
-    constexpr int S = decltype(s)::value;
-    if constexpr (S == 0) return sK0;
-    else if constexpr (S == 1) return sK1;
-    else if constexpr (S == 2) return sK2;
-    else return sK3;
-  };
-  auto slot_v = [&](auto s) __attribute__((always_inline)) -> char* {
-    constexpr int S = decltype(s)::value;
-    if constexpr (S == 0) return sV0;
-    else if constexpr (S == 1) return sV1;
-    else if constexpr (S == 2) return sV2;
-    else return sV3;
-  };
-
-  // block n sits in slot S; block n + kSlots - 1 is loaded into the slot
-  // that block n - 1 used.  The ring is unrolled over its slots so that the
-  // compiler sees which LDS object each read and each load touches.
-  auto stage = [&](auto s, int n) __attribute__((always_inline)) {
-    constexpr int S = decltype(s)::value;
-    constexpr int SN = (S + kSlots - 1) % kSlots;
-    if constexpr (kSlots == 2) {
-      wait_vm<0>();                                      // block n has landed
-    } else {
-      const int ahead = min(kSlots - 2, nblk - 1 - n);   // blocks issued after n
-      if (ahead >= 2) wait_vm<16>();
-      else if (ahead == 1) wait_vm<8>();
-      else wait_vm<0>();
-    }
-    __builtin_amdgcn_s_barrier();      // ... for every wave; slot SN is free
-    if (n + kSlots - 1 < nblk) issue(n + kSlots - 1, slot_k(slot_c<SN>{}), slot_v(slot_c<SN>{}));
-    compute(n, slot_k(s), slot_v(s));
+  // block n sits in one slot while block n + 1 is loaded into the other.
+  // The loop is unrolled over the two slots so that the compiler sees which
+  // LDS object each read and each load touches.
+  auto stage = [&](int n, const char* kt, const char* vt, char* kn, char* vn)
+                   __attribute__((always_inline)) {
+    wait_vm<0>();                      // block n has landed ...
+    __builtin_amdgcn_s_barrier();      // ... for every wave; the other slot is free
+    if (n + 1 < nblk) issue(n + 1, kn, vn);
+    compute(n, kt, vt);
   };
 
   if (nblk > 0) issue(0, sK0, sV0);
-  if constexpr (kSlots == 4) {
-    if (nblk > 1) issue(1, sK1, sV1);
-    if (nblk > 2) issue(2, sK2, sV2);
-  }
-  for (int n = 0; n < nblk; n += kSlots) {
-    stage(slot_c<0>{}, n);
-    if (n + 1 < nblk) stage(slot_c<1>{}, n + 1);
-    if constexpr (kSlots == 4) {
-      if (n + 2 < nblk) stage(slot_c<2>{}, n + 2);
-      if (n + 3 < nblk) stage(slot_c<3>{}, n + 3);
-    }
+  for (int n = 0; n < nblk; n += 2) {
+    stage(n, sK0, sV0, sK1, sV1);
+    if (n + 1 < nblk) stage(n + 1, sK1, sV1, sK0, sV0);
   }
   wait_vm<0>();                                          // no load lands after the end
 
@@ -453,27 +413,33 @@ __global__ __launch_bounds__(256, kOcc) void swa_attn_kernel(AttnArgs a) {
 // Merge the key splits of each (sequence, token, head) in split order:
 // o = sum_s 2^(m_s - m) o_s / sum_s 2^(m_s - m) l_s with m = max_s m_s.  A
 // split that saw no key of the row has l_s = 0 and o_s = 0 and weighs 0.
+// kSplits is a compile-time count, so every load is issued before the first
+// use and the merge costs one memory latency.
+template <int kSplits>
 __global__ __launch_bounds__(128) void swa_combine_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
-                                                          int rows, int splits, void* out,
-                                                          int out_f32) {
+                                                          int rows, void* out, int out_f32) {
   const int row = blockIdx.x;
   const int d = threadIdx.x;
   if (row >= rows) return;
-  const float* ml = part_ml + (int64_t)row * splits * 2;
-  const float* po = part_o + (int64_t)row * splits * kHd + d;
-  float mmax = -1e30f;
-  for (int s = 0; s < splits; ++s) {
-    const float ms = ml[2 * s], ls = ml[2 * s + 1];
-    mmax = ls > 0.f ? fmaxf(mmax, ms) : mmax;
+  const float* ml = part_ml + (int64_t)row * kSplits * 2;
+  const float* po = part_o + (int64_t)row * kSplits * kHd + d;
+  float ms[kSplits], ls[kSplits], os[kSplits];
+#pragma unroll
+  for (int s = 0; s < kSplits; ++s) {
+    ms[s] = ml[2 * s];
+    ls[s] = ml[2 * s + 1];
+    os[s] = po[(int64_t)s * kHd];
   }
+  float mmax = -1e30f;
+#pragma unroll
+  for (int s = 0; s < kSplits; ++s) mmax = ls[s] > 0.f ? fmaxf(mmax, ms[s]) : mmax;
   float num = 0.f, den = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < splits; ++s) {
-    const float ms = ml[2 * s], ls = ml[2 * s + 1];
-    const float w = ls > 0.f ? __builtin_amdgcn_exp2f(ms - mmax) : 0.f;
-    num = __builtin_fmaf(w, po[(int64_t)s * kHd], num);
-    den = __builtin_fmaf(w, ls, den);
+#pragma unroll
+  for (int s = 0; s < kSplits; ++s) {
+    const float w = ls[s] > 0.f ? __builtin_amdgcn_exp2f(ms[s] - mmax) : 0.f;
+    num = __builtin_fmaf(w, os[s], num);
+    den = __builtin_fmaf(w, ls[s], den);
   }
   const float v = den > 0.f ? num / den : 0.f;
   if (out_f32)
@@ -513,30 +479,29 @@ __global__ __launch_bounds__(256) void swa_append_kernel(const bf16_t* __restric
 int swa_head_dim() { return kHd; }
 
 // Launch plan.  Chunks of 64 tokens or more: two 16-token tiles per wave
-// (each K/V fragment read from LDS serves 32 query columns), a 2-slot ring
-// and two workgroups per CU, so that each SIMD runs two waves and the matrix
-// work of one overlaps the softmax of the other.  (Four tiles per wave need
-// more than the 256 registers a wave has at that occupancy; at one
-// workgroup per CU they measured slower.)  Shorter chunks (decode): one tile
-// per wave and a 4-slot ring, one workgroup per CU, three blocks of keys in
-// flight.  Key splits are added until the chip is covered (512 resident
-// workgroups, resp. 256), each split at least 4 blocks of 64 keys.
-constexpr int kBigQSub = 2;          // query tiles per wave for chunks of 64 tokens or more
-constexpr int kBigOcc = kBigQSub == 2 ? 2 : 1;
+// (each K/V fragment read from LDS serves 32 query columns); shorter chunks
+// (decode): one tile per wave.  Both run two workgroups per CU, so that each
+// SIMD holds two waves -- the matrix work of one overlaps the softmax of the
+// other, and eight waves per CU keep the loads of decode flowing.  (Measured
+// alternatives: four tiles per wave need more than the 256 registers a wave
+// has at that occupancy and ran slower at one workgroup per CU; decode with
+// one workgroup per CU and 4 or 5 slots in flight was slower than two
+// workgroups with 2 slots.)  Key splits (a power of two, at most 16) are
+// added until 512 workgroups cover the chip, each split at least 4 blocks
+// of 64 keys.
 
 int swa_plan_splits(int B, int T, int W, int H, int KVH, int* qtiles_out, int* qsub_out) {
   const int G = H / KVH;
   const bool big = T >= 64;
-  const int qsub = big ? kBigQSub : 1;
+  const int qsub = big ? 2 : 1;
   const int wg_tokens = 16 * qsub * (kWaves / G);
   const int qtiles = (T + wg_tokens - 1) / wg_tokens;
   const int64_t wgs = (int64_t)B * KVH * qtiles;
-  const int64_t target = big ? 256 * kBigOcc : 256;
+  const int64_t target = 512;
   const int keys = min(W, T) + W;                  // generous upper bound of a tile's range
-  const int max_splits = max(1, keys / (4 * kKB));
-  int splits = 1;
-  while (splits < max_splits && wgs * splits < target) splits *= 2;
-  splits = min(splits, max_splits);
+  const int max_splits = min(16, max(1, keys / (4 * kKB)));
+  int splits = 1;                                  // a power of two, at most 16
+  while (2 * splits <= max_splits && wgs * splits < target) splits *= 2;
   if (qtiles_out) *qtiles_out = qtiles;
   if (qsub_out) *qsub_out = qsub;
   return splits;
@@ -570,15 +535,23 @@ hipError_t launch_swa_attention(const void* q, const void* k_new, const void* v_
   const int64_t grid = (int64_t)B * KVH * qtiles * splits;
   if (grid == 0) return hipSuccess;
   if (qsub == 1)
-    hipLaunchKernelGGL((swa_attn_kernel<1, 4, 1>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(swa_attn_kernel<1>, dim3((unsigned)grid), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((swa_attn_kernel<kBigQSub, 2, kBigOcc>), dim3((unsigned)grid), dim3(256), 0,
-                       stream, a);
+    hipLaunchKernelGGL(swa_attn_kernel<2>, dim3((unsigned)grid), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   const int rows = B * T * H;
-  hipLaunchKernelGGL(swa_combine_kernel, dim3(rows), dim3(kHd), 0, stream, part_o, part_ml, rows,
-                     splits, out, out_f32);
+  switch (splits) {
+    case 2: hipLaunchKernelGGL(swa_combine_kernel<2>, dim3(rows), dim3(kHd), 0, stream, part_o,
+                               part_ml, rows, out, out_f32); break;
+    case 4: hipLaunchKernelGGL(swa_combine_kernel<4>, dim3(rows), dim3(kHd), 0, stream, part_o,
+                               part_ml, rows, out, out_f32); break;
+    case 8: hipLaunchKernelGGL(swa_combine_kernel<8>, dim3(rows), dim3(kHd), 0, stream, part_o,
+                               part_ml, rows, out, out_f32); break;
+    case 16: hipLaunchKernelGGL(swa_combine_kernel<16>, dim3(rows), dim3(kHd), 0, stream, part_o,
+                                part_ml, rows, out, out_f32); break;
+    default: return hipErrorInvalidValue;   // the plan only makes powers of two up to 16
+  }
   return hipGetLastError();
 }
 
