@@ -84,6 +84,8 @@ CASES = [
     dict(B=1, T=64, W=64, H=4, KVH=1, pos0=(1,)),               # one kv head for 4 heads
     dict(B=2, T=1, W=1, H=4, KVH=1, pos0=(0, 9)),               # W = 1: each token alone
     dict(B=1, T=2, W=2, H=8, KVH=2, pos0=(5,)),                 # W = 2, chunk = W
+    dict(B=8, T=1, W=512, H=32, KVH=8, pos0=(700,) * 4 + (100,) * 4),    # 2 key splits
+    dict(B=8, T=1, W=1024, H=32, KVH=8, pos0=(5000,) * 4 + (1023,) * 4),  # 4 key splits
 ]
 
 
