@@ -5,9 +5,10 @@
 // to -inf, so the softmax runs over the K selected logits only).
 //
 // TPT threads per token (64 or 256).  Each thread accumulates fp32 partial
-// logits over a strided set of 8-wide k chunks; partials are combined by a
-// butterfly inside each wavefront and then across the token's wavefronts in
-// wave order (fixed order: deterministic).  In the vector path (bf16,
+// logits over a strided set of 8-wide k chunks; the 8 partials of a block
+// of experts are combined by one transposed butterfly inside each wavefront
+// and then across the token's wavefronts in wave order (fixed order:
+// deterministic).  In the vector path (bf16,
 // E % 8 == 0, d % 8 == 0) a chunk is one 16-byte load of x and eight 16-byte
 // loads of the matching W_g rows.  Selection takes K rounds of a wave-wide
 // arg-max with key (-logit, index), so equal logits go to the lower index.
@@ -29,9 +30,26 @@ __device__ __forceinline__ float load_f<bf16_t>(const bf16_t* p, int64_t i) {
   return bf16_to_f32(p[i]);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
+// Sum 8 per-lane partials over the wavefront in 10 exchanges: at each of
+// the strides 32, 16, 8 a lane keeps half of its values and adds its
+// partner's copy of them, so afterwards lane l holds value
+// e(l) = 4 bit5(l) + 2 bit4(l) + bit3(l) = l / 8 summed over its stride
+// partners, and strides 4, 2, 1 finish the sum.  Every lane of a group of
+// 8 ends with the same bits (each addition is commutative).
+__device__ __forceinline__ float wave_sum8(const float (&a)[8], int lane) {
+  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+  float v4[4];
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  for (int j = 0; j < 4; ++j)
+    v4[j] = (b5 ? a[j + 4] : a[j]) + __shfl_xor(b5 ? a[j] : a[j + 4], 32, 64);
+  float v2[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    v2[j] = (b4 ? v4[j + 2] : v4[j]) + __shfl_xor(b4 ? v4[j] : v4[j + 2], 16, 64);
+  float v = (b3 ? v2[1] : v2[0]) + __shfl_xor(b3 ? v2[0] : v2[1], 8, 64);
+  v += __shfl_xor(v, 4, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 1, 64);
   return v;
 }
 
@@ -77,6 +95,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const T* __restrict__ 
     for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
     if (live) {
       if constexpr (VEC) {
+#pragma unroll 4
         for (int k0 = sub * 8; k0 < d; k0 += TPT * 8) {
           float xv[8];
           bf16x8_to_f32(*reinterpret_cast<const uint4*>(xr + k0), xv);
@@ -98,11 +117,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const T* __restrict__ 
         }
       }
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float s = wave_sum(acc[j]);
-      if (lane == 0 && e0 + j < E) wave_part[wave][e0 + j] = s;
-    }
+    const float s = wave_sum8(acc, lane);              // value lane / 8
+    if ((lane & 7) == 0 && e0 + (lane >> 3) < E) wave_part[wave][e0 + (lane >> 3)] = s;
   }
   __syncthreads();
   // Combine the token's waves in order; lane e of the token's first wave keeps logit e.
