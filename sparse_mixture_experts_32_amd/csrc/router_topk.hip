@@ -163,6 +163,97 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const T* __restrict__ 
     for (int r = 0; r < K; ++r) out_w[r] = out_w[r] / denom;
 }
 
+// Many tokens, 8 experts, bf16: each wavefront takes 4 tokens, so every
+// 16-byte piece of W_g it loads serves 4 tokens (a token per wavefront would
+// read all of W_g once per token).  Lane l accumulates the 8-wide feature
+// chunks l, l + 64, ... of each token; after the transposed butterfly lane
+// l holds expert l / 8 of each token.  Top-K then runs for the 4 tokens at
+// once: lane 16 n + e (e < 8) holds expert e of token n, and K rounds of an
+// arg-max over each 16-lane group pick the experts with key (-logit, index),
+// as in the general kernel.
+constexpr int kRouterTokPerWave = 4;
+
+__global__ __launch_bounds__(256) void router_e8_kernel(const bf16_t* __restrict__ x,
+                                                        const bf16_t* __restrict__ Wg, int T_,
+                                                        int d, int K,
+                                                        int32_t* __restrict__ topk_idx,
+                                                        float* __restrict__ topk_w,
+                                                        float* __restrict__ logits_out) {
+  constexpr int NT = kRouterTokPerWave;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t0 = (blockIdx.x * 4 + wave) * NT;         // first token of this wavefront
+  if (t0 >= T_) return;                                 // wave-uniform; no barriers below
+  const bf16_t* xr[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) xr[n] = x + (int64_t)min(t0 + n, T_ - 1) * d;
+  float acc[NT][8];
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[n][j] = 0.0f;
+#pragma unroll 2
+  for (int k0 = lane * 8; k0 < d; k0 += 64 * 8) {
+    float wv[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      bf16x8_to_f32(*reinterpret_cast<const uint4*>(Wg + (int64_t)(k0 + i) * 8), wv[i]);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      float xv[8];
+      bf16x8_to_f32(*reinterpret_cast<const uint4*>(xr[n] + k0), xv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[n][j] = fmaf(xv[i], wv[i][j], acc[n][j]);
+    }
+  }
+  float lg[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) lg[n] = wave_sum8(acc[n], lane);   // expert lane / 8
+  if (logits_out && (lane & 7) == 0) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      if (t0 + n < T_) logits_out[(int64_t)(t0 + n) * 8 + (lane >> 3)] = lg[n];
+  }
+  // lane 16 n + e: expert e of token n (e < 8; lanes with e >= 8 hold nothing)
+  const int n = lane >> 4;
+  const int e = lane & 15;
+  float v = 0.0f;
+#pragma unroll
+  for (int m = 0; m < NT; ++m) {
+    const float g = __shfl(lg[m], 8 * (e & 7), 64);
+    if (m == n) v = g;
+  }
+  const bool live = t0 + n < T_;
+  bool taken = false;
+  float first = 0.0f, denom = 0.0f;
+  const int64_t t = t0 + n;
+  for (int r = 0; r < K; ++r) {
+    float bv = v;
+    int bi = (e < 8 && !taken) ? e : -1;
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      const float ov = __shfl_xor(bv, m, 64);
+      const int oi = __shfl_xor(bi, m, 64);
+      if (ranks_before(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (e == bi) taken = true;
+    if (r == 0) first = bv;
+    const float ex = expf(bv - first);
+    denom += ex;
+    if (e == 0 && live) {
+      topk_idx[t * K + r] = bi;
+      topk_w[t * K + r] = ex;
+    }
+  }
+  if (e == 0 && live)
+    for (int r = 0; r < K; ++r) topk_w[t * K + r] = topk_w[t * K + r] / denom;
+}
+
 template <typename T, int TPT, bool VEC>
 void launch_t(const void* x, const void* Wg, int T_, int d, int E, int K, int32_t* idx,
               float* w, float* logits, hipStream_t stream) {
@@ -182,6 +273,13 @@ hipError_t launch_router_topk(const void* x, const void* Wg, int T, int d, int E
   const bool vec = dtype == kBF16 && E % 8 == 0 && d % 8 == 0 &&
                    (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(Wg) & 15) == 0;
+  if (dtype == kBF16 && vec && !wide && E == 8 && K <= 8) {
+    const int per_block = 4 * kRouterTokPerWave;
+    hipLaunchKernelGGL(router_e8_kernel, dim3((T + per_block - 1) / per_block), dim3(256), 0,
+                       stream, static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(Wg), T, d,
+                       K, topk_idx, topk_w, logits);
+    return hipGetLastError();
+  }
   if (dtype == kBF16) {
     if (vec) {
       if (wide) launch_t<bf16_t, 256, true>(x, Wg, T, d, E, K, topk_idx, topk_w, logits, stream);

@@ -99,28 +99,31 @@ def check_layer(inp, K, tokens=None, bf16_store=True):
 
 
 # ---------------------------------------------------------------- router
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_router_small(dev, dtype):
-    w = small(T=300, d=256, d_ff=128, dtype=dtype)
-    say("router", dtype, w.T, w.d)
+# T >= 1024 with 8 experts takes the many-token router (4 tokens per wavefront)
+@pytest.mark.parametrize("dtype,T,K", [("bf16", 300, 2), ("f32", 300, 2), ("bf16", 1500, 2),
+                                       ("bf16", 1027, 1), ("bf16", 1100, 4), ("f32", 1100, 2)])
+def test_router_small(dev, dtype, T, K):
+    w = small(T=T, d=256, d_ff=128, dtype=dtype)
+    say("router", dtype, w.T, w.d, K)
     W_g, _, _, _ = W.expert_weights(w, dev, experts=[])
     x = W.make_x(w, W_g, dev)
     logits = torch.empty((w.T, w.E), dtype=torch.float32, device=dev)
-    idx, wt = M.moe_router_topk(x, W_g, 2, logits=logits)
+    idx, wt = M.moe_router_topk(x, W_g, K, logits=logits)
     torch.cuda.synchronize()
     l64 = O.router_logits(PY.to_np(x), PY.to_np(W_g))
     assert np.abs(PY.to_np(logits) - l64).max() <= 1e-5 * (1 + np.abs(l64).max())
-    ref_idx = O.topk_select(l64, 2)
+    ref_idx = O.topk_select(l64, K)
     PY.check_routing(idx.cpu().numpy(), wt.cpu().numpy(), ref_idx, O.gate_weights(l64, ref_idx),
-                     l64, 2)
+                     l64, K)
 
 
-def test_router_ties_lower_index_wins(dev):
+@pytest.mark.parametrize("T", [512, 1100])
+def test_router_ties_lower_index_wins(dev, T):
     """Columns 5 and 7 of W_g copy column 2, so logits 2, 5, 7 tie exactly (in
     fp32 on the GPU and in float64 in the oracle).  Where the distinct logit
     values around the selection are more than 1e-3 apart, the GPU must make
     the oracle's choice, which resolves the tie towards the lower index."""
-    w = small(T=512, d=128, d_ff=128, E=8)
+    w = small(T=T, d=128, d_ff=128, E=8)
     say("router ties")
     W_g, _, _, _ = W.expert_weights(w, dev, experts=[])
     W_g[:, 5] = W_g[:, 2]
