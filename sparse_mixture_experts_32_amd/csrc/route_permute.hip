@@ -3,14 +3,14 @@
 // ("从Mistral 7B到MoE模型Mixtral 8x7B的全面解析" (aiqianji.com) section 3.1.2 and
 // code blocks B, C: for every expert, the list of pairs routed to it).
 //
-// One workgroup of 1024 threads.  Pass 1 counts pairs per expert with LDS
-// integer atomics (the counts do not depend on the order).  Thread 0 scans
-// the E counts.  Pass 2 walks the pairs in rounds of 1024 in pair order
-// p = t*K + r; inside a round a wavefront ranks its lanes per expert with one
-// ballot per expert, waves are ordered by their index, and a per-expert
-// running count carries across rounds.  So the destination of pair p is
+// One workgroup of 1024 threads computes, for pair p = t*K + r routed to
+// expert e, the destination
 //   offsets[e] + #{p' < p : idx[p'] = e},
-// a stable counting sort: bit-exact and deterministic.
+// a stable counting sort: bit-exact and deterministic.  Two forms: from
+// 2049 to 16384 pairs and up to 16 experts, the pairs are held in registers
+// and counted per (round of 1024, wavefront) at once; otherwise they stream
+// through in rounds (LDS atomics for the histogram, then one ranking pass
+// per round).
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -21,6 +21,10 @@ namespace {
 constexpr int kPermuteThreads = 1024;
 constexpr int kPermuteWaves = kPermuteThreads / 64;
 
+// Streaming form (any P): rounds of 1024 pairs in pair order; inside a
+// round a wavefront ranks its lanes per expert with one ballot per expert,
+// waves are ordered by their index, and a per-expert running count carries
+// across rounds.
 __global__ __launch_bounds__(kPermuteThreads) void route_permute_kernel(
     const int32_t* __restrict__ topk_idx, int P, int E, int K, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_token, int32_t* __restrict__ pos) {
@@ -81,12 +85,112 @@ __global__ __launch_bounds__(kPermuteThreads) void route_permute_kernel(
   }
 }
 
+// Held form (P <= R * 1024, E <= 16): every pair is loaded once into
+// registers; the pairs of round j, wave w that go to expert x are counted
+// with one ballot (cnt[x][j * 16 + w], in pair order along the second
+// index); one wavefront per expert turns its row into an exclusive prefix
+// (lane l sums R/4 consecutive entries, then a wave-wide scan); thread 0
+// scans the expert totals.  Destination of a pair: offsets[x] + prefix of
+// its (round, wave) + its rank among the lanes of its wave -- the same
+// stable counting sort as the streaming form, with three barriers in all.
+template <int R>
+__global__ __launch_bounds__(kPermuteThreads) void route_permute_held_kernel(
+    const int32_t* __restrict__ topk_idx, int P, int E, int K, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_token, int32_t* __restrict__ pos) {
+  constexpr int kMaxE = 16;
+  constexpr int kCols = R * kPermuteWaves;          // (round, wave) slots per expert
+  static_assert(kCols % 64 == 0 || kCols < 64, "whole lanes per slot group");
+  __shared__ int cnt[kMaxE][kCols];
+  __shared__ int total[kMaxE];
+  __shared__ int offs[kMaxE + 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const uint64_t lower_lanes = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+  int held[R], rank[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int p = j * kPermuteThreads + tid;
+    const int e = p < P ? topk_idx[p] : -1;
+    held[j] = (e >= 0 && e < E) ? e : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    rank[j] = 0;
+    for (int x = 0; x < E; ++x) {
+      const uint64_t m = __ballot(held[j] == x);
+      if (lane == 0) cnt[x][j * kPermuteWaves + wave] = __popcll(m);
+      if (held[j] == x) rank[j] = __popcll(m & lower_lanes);
+    }
+  }
+  __syncthreads();
+  // exclusive prefix of each expert's row, one wavefront per expert
+  if (wave < E) {
+    constexpr int kPer = kCols >= 64 ? kCols / 64 : 1;   // entries per lane
+    int vals[kPer];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = lane * kPer + i;
+      vals[i] = c < kCols ? cnt[wave][c] : 0;
+      sum += vals[i];
+    }
+    int incl = sum;                                       // inclusive scan over lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = lane * kPer + i;
+      if (c < kCols) cnt[wave][c] = run;
+      run += vals[i];
+    }
+    if (lane == 63) total[wave] = incl;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    offs[0] = 0;
+    for (int e = 0; e < E; ++e) offs[e + 1] = offs[e] + total[e];
+  }
+  __syncthreads();
+  if (tid <= E) offsets[tid] = offs[tid];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int p = j * kPermuteThreads + tid;
+    const int e = held[j];
+    if (e >= 0) {
+      const int dest = offs[e] + cnt[e][j * kPermuteWaves + wave] + rank[j];
+      sorted_token[dest] = p / K;
+      pos[p] = dest;
+    } else if (p < P) {
+      pos[p] = -1;  // out-of-range expert index: the pair is dropped
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_route_permute(const int32_t* topk_idx, int T, int E, int K, int32_t* offsets,
                                 int32_t* sorted_token, int32_t* pos, hipStream_t stream) {
-  hipLaunchKernelGGL(route_permute_kernel, dim3(1), dim3(kPermuteThreads), 0, stream, topk_idx,
-                     T * K, E, K, offsets, sorted_token, pos);
+  const int P = T * K;
+  const int rounds = (P + kPermuteThreads - 1) / kPermuteThreads;
+#define MOE_PERMUTE_HELD(R)                                                                 \
+  hipLaunchKernelGGL(route_permute_held_kernel<R>, dim3(1), dim3(kPermuteThreads), 0, stream, \
+                     topk_idx, P, E, K, offsets, sorted_token, pos)
+  // one or two rounds stream faster than the held form's fixed four
+  const bool held = E <= 16 && rounds >= 3 && rounds <= 16;
+  if (held && rounds <= 4) MOE_PERMUTE_HELD(4);
+  else if (held && rounds <= 8) MOE_PERMUTE_HELD(8);
+  else if (held) MOE_PERMUTE_HELD(16);
+  else
+    hipLaunchKernelGGL(route_permute_kernel, dim3(1), dim3(kPermuteThreads), 0, stream, topk_idx,
+                       P, E, K, offsets, sorted_token, pos);
+#undef MOE_PERMUTE_HELD
   return hipGetLastError();
 }
 

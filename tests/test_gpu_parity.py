@@ -161,8 +161,12 @@ def random_routing(T, E, K, seed, skew=None):
     return torch.argsort(scores, dim=1)[:, :K]
 
 
+# pairs held in registers for 2048 < P <= 16384 and E <= 16 (4, 8 or 16
+# rounds of 1024), streamed otherwise
 @pytest.mark.parametrize("T,E,K", [(1, 8, 2), (7, 8, 2), (1000, 8, 2), (5000, 8, 2),
-                                   (333, 64, 4), (64, 1, 1), (129, 8, 8), (2048, 16, 1)])
+                                   (333, 64, 4), (64, 1, 1), (129, 8, 8), (2048, 16, 1),
+                                   (1500, 8, 2), (3000, 16, 2), (8192, 8, 2), (9000, 8, 2),
+                                   (1100, 32, 3)])
 def test_permute_bit_exact(dev, T, E, K):
     say("permute", T, E, K)
     idx = random_routing(T, E, K, seed=T * 131 + E * 7 + K)
