@@ -86,6 +86,8 @@ CASES = [
     dict(B=1, T=2, W=2, H=8, KVH=2, pos0=(5,)),                 # W = 2, chunk = W
     dict(B=8, T=1, W=512, H=32, KVH=8, pos0=(700,) * 4 + (100,) * 4),    # 2 key splits
     dict(B=8, T=1, W=1024, H=32, KVH=8, pos0=(5000,) * 4 + (1023,) * 4),  # 4 key splits
+    dict(B=1, T=128, W=2048, H=32, KVH=8, pos0=(3000,)),      # two tiles per wave + key splits
+    dict(B=1, T=1, W=32768, H=8, KVH=2, pos0=(100000,)),      # large window, 16 key splits
 ]
 
 
