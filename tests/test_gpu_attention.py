@@ -116,6 +116,28 @@ def test_attention_deterministic(dev):
     assert torch.equal(a, b)
 
 
+def test_workspace_reused_across_shapes(dev):
+    """One workspace serves shapes with different split counts and tile grids
+    in turn (each call overwrites what the previous left): every output
+    equals the call with a fresh workspace bit for bit."""
+    shapes = [small(B=8, T=1, W=4096, H=32, KVH=8, pos0=(8191,) * 8),     # 8 splits
+              small(B=2, T=1, W=4096, H=8, KVH=2, pos0=(5000, 10)),       # 16 splits
+              small(B=1, T=128, W=2048, H=32, KVH=8, pos0=(3000,)),       # two-tile kernel
+              small(B=8, T=1, W=1024, H=32, KVH=8, pos0=(5000,) * 8)]     # 4 splits
+    need = max(M.swa_workspace_size(w.B, w.T, w.W, w.H, w.KVH) for w in shapes)
+    ws = torch.full((need,), 0x7f, dtype=torch.uint8, device=dev)   # not zero on purpose
+    for w in shapes + shapes[:1]:
+        say("shared workspace", w.B, w.T, w.W, w.H, w.KVH)
+        assert M.swa_workspace_size(w.B, w.T, w.W, w.H, w.KVH) > 0
+        inp = W.attn_inputs(w, dev)
+        args = (inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], inp["pos0"],
+                w.W)
+        shared = M.swa_attention(*args, out_dtype=torch.float32, workspace=ws)
+        fresh = M.swa_attention(*args, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(shared, fresh)
+
+
 def test_cache_append_bit_exact(dev):
     for T, Wn, pos in [(5, 16, (14, 0)), (20, 16, (3, 30)), (1, 4096, (8191, 4096))]:
         w = small(B=2, T=T, W=Wn, H=4, KVH=2, pos0=pos)
