@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 #define MOE_MAX_EXPERTS 64
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -61,7 +61,9 @@ typedef enum {
  * so a caller of the stages runs exactly the kernels moe_forward runs.
  */
 typedef struct moe_plan {
-  int32_t swiglu_splits;        /* K splits of the W1/W3 product (1 = fused epilogue)   */
+  int32_t swiglu_splits;        /* W1/W3 product: 0 = fused (writes H itself); s >= 1 =  */
+                                /* fp32 partial sums over s K slices per matrix, which  */
+                                /* moe_swiglu_finish completes                          */
   int32_t down_splits;          /* K splits of the W2 product = slices of O             */
   size_t swiglu_scratch_bytes;  /* fp32 partial sums the W1/W3 product needs (0 if none) */
   int32_t streaming;            /* 1: weight-streaming (small batch) kernels, 0: tiled   */
@@ -159,9 +161,10 @@ moe_status moe_route_permute(const int32_t* topk_idx, int64_t T, int32_t E, int3
  * expert e, H[r] = round(SiLU(x[sorted_token[r]] W1[e]) * (x[...] W3[e])),
  * fp32 accumulation, one rounding to dtype.  H [T*K, d_ff] in dtype.
  * scratch: device buffer of plan.swiglu_scratch_bytes (may be NULL when that
- * is 0); MOE_EWORKSPACE if smaller.  With plan.swiglu_splits > 1 this call
- * leaves fp32 partial sums over K slices in scratch and moe_swiglu_finish
- * writes H; with one split it writes H itself.
+ * is 0); MOE_EWORKSPACE if smaller.  With plan.swiglu_splits > 0 this call
+ * leaves fp32 partial sums of both products over K slices in scratch and
+ * moe_swiglu_finish writes H; with plan.swiglu_splits == 0 it writes H
+ * itself.
  */
 moe_status moe_expert_swiglu(const void* x, const void* const* W1, const void* const* W3,
                              int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K,
@@ -169,10 +172,10 @@ moe_status moe_expert_swiglu(const void* x, const void* const* W1, const void* c
                              void* H, void* scratch, size_t scratch_bytes, void* stream);
 
 /*
- * Completes step 6 when plan.swiglu_splits > 1 (small batches): the fp32
+ * Completes step 6 when plan.swiglu_splits > 0 (small batches): the fp32
  * partial sums that moe_expert_swiglu left in `scratch` are added in split
- * order and H = round(SiLU(a) * b) is written.  With one split H is already
- * complete and this call does nothing (MOE_OK).
+ * order and H = round(SiLU(a) * b) is written.  With plan.swiglu_splits == 0
+ * H is already complete and this call does nothing (MOE_OK).
  */
 moe_status moe_swiglu_finish(const void* scratch, int64_t T, int64_t d, int64_t d_ff, int32_t E,
                              int32_t K, int32_t dtype, void* H, void* stream);

@@ -40,11 +40,19 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-# Per-file additions.  The attention kernels take finite inputs by contract
-# (infinities are used as mask values, NaNs never arise), so the compiler may
-# drop the NaN-quieting operand moves it otherwise places before each
-# floating-point max of the softmax.
-FILE_FLAGS = {"swa_attention.hip": ["-fno-honor-nans"]}
+# Per-file additions.
+# * The attention kernels take finite inputs by contract (infinities are used
+#   as mask values, NaNs never arise), so the compiler may drop the
+#   NaN-quieting operand moves it otherwise places before each floating-point
+#   max of the softmax.
+# * The weight-streaming kernels keep their matrix accumulators in ordinary
+#   vector registers: left to choose, the register allocator moved them
+#   between accumulator and vector registers on every k-step, which took the
+#   kernel to one wave per SIMD.
+FILE_FLAGS = {
+    "swa_attention.hip": ["-fno-honor-nans"],
+    "expert_stream_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _compile(src: str) -> str:

@@ -5,27 +5,46 @@
 // Same product as the LDS-tiled kernels ("从Mistral 7B到MoE模型Mixtral 8x7B
 // 的全面解析" (aiqianji.com) section 3.2.4, code block D), organised for
 // bandwidth:
-//   * a wavefront owns 128 features and a k-range; each lane fetches an 8x8
-//     (k x feature) block with eight 16-byte loads per weight matrix, lanes
-//     0-15 covering 256 contiguous bytes of one weight row;
-//   * the block is transposed in registers and used directly as the M-side
-//     operand of v_mfma_f32_16x16x32_bf16 (instruction c takes feature
-//     8*i + c at M-row i) -- no LDS round trip for the weights;
-//   * the token operand (16 rows x 8 k per lane) is a 16-byte load of the
-//     gathered activation row, L2-resident;
+//   * a wavefront owns 256 features and a k-range.  Every 16-byte load
+//     instruction covers two 512-byte row segments: lanes 0-31 read 512
+//     contiguous bytes of one weight row, lanes 32-63 the same columns eight
+//     rows further down.  (Measured with a loads-only replica, two 512-byte
+//     segments per instruction stream at ~6.9 TB/s, four 256-byte segments
+//     at ~6.4 TB/s.)
+//   * a k-step of 32 rows takes 16 loads per lane: rows 0-7 and 16-23 of the
+//     step for lanes 0-31, 8-15 and 24-31 for lanes 32-63.  Each group of 8
+//     loads is transposed in registers (v_perm_b32) into 8-k columns of one
+//     feature; v_permlane16_swap then regroups the 16-lane rows so that one
+//     register holds features 0-127 of the wave over four k-groups and the
+//     other features 128-255.  Each is the M-side operand of
+//     v_mfma_f32_16x16x32_bf16 (instruction c takes feature 8*i + c at
+//     M-row i); no LDS round trip for the weights.  The k-groups sit in the
+//     operand in the order 0, 16, 8, 24, and the token operand (16 rows x 8
+//     k per lane, a 16-byte load of the gathered activation row, L2-resident)
+//     follows the same order;
 //   * loads for the next k-step are issued before the current step's
-//     transposes and matrix instructions (two register stages);
-//   * every wave streams one matrix: with two matrices (W1, W3) waves 0-1
-//     take W1 and waves 2-3 take W3, each pair splitting the k-range; with
-//     one matrix the four waves split it.  The waves' partial products are
-//     summed in LDS in wave order;
-//   * K is further split over `splits` workgroups (fp32 partial sums written
-//     to separate slices, summed later in slice order), so results are
-//     deterministic and the grid has thousands of workgroups.
-// Epilogue: with one split and two matrices, H = bf16(SiLU(a) * b) is
-// stored directly; otherwise the fp32 partial sums are stored and
-// swiglu_finish_kernel (its own launch) adds the splits in order and applies
-// SwiGLU.
+//     transposes and matrix instructions (two register stages).  The k loop is
+//     straight-line (no data-dependent branch: padding rows of a token tile
+//     load a real row), so the wait before a step covers only that step's
+//     loads;
+//   * a workgroup has eight waves (two per SIMD, one workgroup per compute
+//     unit) and every wave streams one matrix.  The W2 product puts all
+//     eight on W2, splitting the workgroup's k-range eight ways.  The W1/W3
+//     product runs one of two ways (StreamMode): fused -- waves 0-3 on W1,
+//     4-7 on W3, each four splitting the whole of K, and H = bf16(SiLU(a) *
+//     b) stored by the epilogue -- or per matrix -- W1 and W3 in alternate
+//     workgroups, K split over `splits` workgroups, fp32 partial sums of a
+//     and b stored for swiglu_finish_kernel (its own launch), which adds the
+//     slices in order and applies SwiGLU.  The waves' partial products meet
+//     in LDS and are added in wave order;
+//   * K splits write fp32 partial sums to separate slices (non-temporal
+//     stores), summed later in slice order, so results are deterministic.
+//     Every partial byte written costs streaming time -- a loads-only
+//     replica slowed by 13 % when its workgroups also wrote 1.6 % as many
+//     bytes as they read -- so the launch form and split count are chosen
+//     per batch size by how the workgroups fill the chip (pick_launch), and
+//     a per-matrix W1/W3 split writes half the partial bytes of a split
+//     fused one for the same grid.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -39,8 +58,8 @@ struct StreamArgs {
   const int32_t* offsets;  // [E + 1]
   ExpertPtrs Wa;
   ExpertPtrs Wb;
-  bf16_t* H;               // final H when DUAL and splits == 1
-  float* part;             // [splits][mats][P][N] partial sums otherwise
+  bf16_t* H;               // H of the fused W1/W3 launch
+  float* part;             // [splits][slices][P][N] partial sums otherwise
   int Kdim;
   int N;
   int E;
@@ -58,8 +77,8 @@ __device__ __forceinline__ uint32_t perm_hi(uint32_t hi_src, uint32_t lo_src) {
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // rows[r] = 8 bf16 of k-row r (features c = 0..7, two per dword); returns
-// operand c = the 8 k-values of feature c.
-__device__ __forceinline__ bf16x8_t column(const u32x4_t rows[8], int c) {
+// the 8 k-values of feature c.
+__device__ __forceinline__ u32x4_t column(const u32x4_t* rows, int c) {
   const int q = c >> 1;
   u32x4_t v;
   if ((c & 1) == 0) {
@@ -73,145 +92,226 @@ __device__ __forceinline__ bf16x8_t column(const u32x4_t rows[8], int c) {
     v[2] = perm_hi(rows[5][q], rows[4][q]);
     v[3] = perm_hi(rows[7][q], rows[6][q]);
   }
-  return __builtin_bit_cast(bf16x8_t, v);
+  return v;
 }
 
-constexpr int kWaves = 4;
-constexpr int kFeat = 128;  // features per workgroup (and per wave)
+// Buffer resource word 3 of the gfx9 family (32-bit data format, so untyped
+// loads return data), and the cache-policy bit of a non-temporal load.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kNonTemporal = 2;
 
-template <int NJ, bool DUAL>
+constexpr int kWaves = 8;           // waves per workgroup (two per SIMD)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kFeat = kStreamFeat;  // features per workgroup (and per wave)
+// The launch choice (pick_launch) counts rounds of workgroups over the
+// chip's 256 compute units.  Measured at 1-32 tokens (MI355X, every split
+// count timed): a single round that fills at least ~55 % of the compute
+// units beats more, shorter workgroups; without one, an unsplit product of
+// at least 1.7 rounds (no partial sums, no finish launch) beats splitting,
+// and otherwise about three rounds do best.  For Mixtral's shapes at 1, 2,
+// 4, 8, 16, 32 tokens this gives W1/W3 per matrix with 1, fused, 2, 1 splits,
+// then fused; W2 with 7, 4, 2, 2, 2, 2 splits.
+constexpr double kComputeUnits = 256;
+constexpr int kLoads = 16;          // 16-byte loads per lane per k-step of 32
+
+// What a launch streams:
+//   kDown:      one matrix (W2); partial sums to O slices.
+//   kFused:     W1 and W3 in every workgroup (waves 0-3 / 4-7), no K split;
+//               H = bf16(SiLU(a) * b) in the epilogue.
+//   kPerMatrix: W1 and W3 in alternate workgroups, all eight waves on one
+//               matrix, K split `splits` ways; fp32 partial sums of a and b
+//               to scratch slices [split][matrix], summed by
+//               swiglu_finish_kernel.  Half the partial-sum bytes of
+//               splitting a fused workgroup's K range for the same grid.
+enum StreamMode { kDown = 0, kFused = 1, kPerMatrix = 2 };
+
+template <int NJ, int MODE>
 struct StreamCfg {
-  static constexpr int kMats = DUAL ? 2 : 1;
-  static constexpr int kKParts = kWaves / kMats;  // waves sharing one matrix
-  // LDS for the wave reduction: [wave][c][j][lane] float4
-  static constexpr int kRedFloats = kWaves * 8 * NJ * 64 * 4;
+  static constexpr int kSlices = MODE == kDown ? 1 : 2;   // partial slices per split
+  static constexpr int kMatsWG = MODE == kFused ? 2 : 1;  // matrices inside a workgroup
+  static constexpr int kKParts = kWaves / kMatsWG;        // waves sharing one matrix
 };
 
-template <int NJ, bool DUAL>
-__global__ __launch_bounds__(256) void stream_gemm_kernel(StreamArgs a) {
-  using C = StreamCfg<NJ, DUAL>;
-  constexpr int M = C::kMats;
-  __shared__ float4 red[C::kRedFloats / 4];
+template <int NJ, int MODE>
+__global__ __launch_bounds__(kThreads) void stream_gemm_kernel(StreamArgs a) {
+  using C = StreamCfg<NJ, MODE>;
+  constexpr int MW = C::kMatsWG;
+  // one feature half (8 accumulators per token tile) of every wave
+  __shared__ f32x4_t red[kWaves * 8 * NJ * 64];
 
   const int tiles_f = a.N / kFeat;
   int bid = blockIdx.x;
+  const int mat_wg = MODE == kPerMatrix ? (bid & 1) : 0;
+  if (MODE == kPerMatrix) bid >>= 1;
   const int ftile = bid % tiles_f;
   bid /= tiles_f;
   const int s = bid % a.splits;
   const int ttile = bid / a.splits;
   int e, row_begin, row_end;
   if (!find_tile(a.offsets, a.E, 16 * NJ, ttile, e, row_begin, row_end)) return;
+  e = __builtin_amdgcn_readfirstlane(e);
+  row_begin = __builtin_amdgcn_readfirstlane(row_begin);
+  row_end = __builtin_amdgcn_readfirstlane(row_end);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int mat = wave / C::kKParts;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int mat = MODE == kPerMatrix ? mat_wg : wave / C::kKParts;
   const int kpart = wave % C::kKParts;
-  const int lrow = lane & 15;
-  const int lk = lane >> 4;
   const int f0 = ftile * kFeat;
   const int kc = a.Kdim / a.splits;
   const int kw = kc / C::kKParts;
   const int kbeg = s * kc + kpart * kw;
   const int nsteps = kw / 32;
   const int64_t N = a.N;
+  const int64_t row_bytes = N * 2;
 
-  const bf16_t* wsrc = static_cast<const bf16_t*>(mat == 0 ? a.Wa.p[e] : a.Wb.p[e]) +
-                       (int64_t)(kbeg + 8 * lk) * N + f0 + 8 * lrow;
-  const bf16_t* bsrc[NJ];
+  // Token operand: lane group g (16 lanes) carries k-group {0, 16, 8, 24}[g]
+  // of the step, matching the weight operand after the lane swap.  Padding
+  // rows (r >= row_end) read the tile's last row: their products land in
+  // output columns that are never stored.
+  const int kofs = 8 * ((lane >> 4) >> 1) + 16 * ((lane >> 4) & 1);
+  int64_t src_row[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int r = row_begin + j * 16 + lrow;
-    bsrc[j] = nullptr;
-    if (r < row_end) {
-      const int64_t src_row = a.gather ? a.gather[r] : r;
-      bsrc[j] = a.A + src_row * a.Kdim + kbeg + 8 * lk;
-    }
+    const int r = min(row_begin + j * 16 + (lane & 15), row_end - 1);
+    src_row[j] = a.gather ? a.gather[r] : r;
   }
 
-  f32x4_t acc[8][NJ];
-#pragma unroll
-  for (int c = 0; c < 8; ++c)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[c][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // Weight loads are buffer loads: a k-step's 32 rows as one resource (base
+  // and size in scalar registers), the row offset in a scalar register, one
+  // 32-bit per-lane offset.  The resource of the step after the last has
+  // size 0, so the loop's final prefetch returns zeros without touching
+  // memory and the loop needs no peeled tail.
+  char* wrow = const_cast<char*>(reinterpret_cast<const char*>(mat == 0 ? a.Wa.p[e] : a.Wb.p[e])) +
+               ((int64_t)kbeg * N + f0) * 2;
+  const int lane_off = (lane >> 5) * 8 * (int)row_bytes + (lane & 31) * 16;
 
-  u32x4_t w0[8], w1[8];
+  f32x4_t acc[2][8][NJ];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[h][c][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  u32x4_t w0[kLoads], w1[kLoads];
   u32x4_t b0[NJ], b1[NJ];
+  const bf16_t* bsrc[NJ];
 
-  auto load = [&](u32x4_t (&w)[8], u32x4_t (&b)[NJ], int step) {
-    const bf16_t* src = wsrc + (int64_t)step * 32 * N;
+  auto load_w = [&](u32x4_t (&w)[kLoads], int step) {
+    const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
+        wrow + (int64_t)step * 32 * row_bytes, (short)0, step < nsteps ? 32 * (int)row_bytes : 0,
+        kBufferWord3);
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-      w[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + (int64_t)r * N));
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      b[j] = bsrc[j] ? *reinterpret_cast<const u32x4_t*>(bsrc[j] + step * 32) : u32x4_t{0, 0, 0, 0};
+    for (int r = 0; r < kLoads; ++r) {
+      const int row = (r & 7) + 16 * (r >> 3);
+      w[r] = __builtin_amdgcn_raw_buffer_load_b128(res, lane_off, row * (int)row_bytes, kNonTemporal);
+    }
   };
-  auto compute = [&](const u32x4_t (&w)[8], const u32x4_t (&b)[NJ]) {
+  auto load_b = [&](u32x4_t (&b)[NJ], int step) {
+    const int st = min(step, nsteps - 1);  // past the end: reread the last step (unused)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) b[j] = *reinterpret_cast<const u32x4_t*>(bsrc[j] + st * 32);
+    // keep the issue here: hoisting the next compute above these loads
+    // would make its wait cover them too
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto compute = [&](const u32x4_t (&w)[kLoads], const u32x4_t (&b)[NJ]) {
     bf16x8_t bo[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) bo[j] = __builtin_bit_cast(bf16x8_t, b[j]);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const bf16x8_t op = column(w, c);
+      // t: k-rows 0-7 (lanes 0-31) / 8-15 (lanes 32-63); u: 16-23 / 24-31.
+      // Lanes 0-15 and 32-47 hold features 0-127, lanes 16-31 and 48-63
+      // features 128-255.
+      const u32x4_t t = column(w, c);
+      const u32x4_t u = column(w + 8, c);
+      u32x4_t lo, hi;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        acc[c][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, bo[j], acc[c][j], 0, 0, 0);
+      for (int v = 0; v < 4; ++v) {
+        const auto r = __builtin_amdgcn_permlane16_swap(t[v], u[v], false, false);
+        lo[v] = r[0];  // rows t0, u0, t2, u2: features 0-127, k-groups 0, 16, 8, 24
+        hi[v] = r[1];  // rows t1, u1, t3, u3: features 128-255, same k-groups
+      }
+      const bf16x8_t opl = __builtin_bit_cast(bf16x8_t, lo);
+      const bf16x8_t oph = __builtin_bit_cast(bf16x8_t, hi);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        acc[0][c][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(opl, bo[j], acc[0][c][j], 0, 0, 0);
+        acc[1][c][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oph, bo[j], acc[1][c][j], 0, 0, 0);
+      }
+      // one column at a time: forming all eight operands first would hold
+      // 64 more registers
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  if (nsteps > 0) load(w0, b0, 0);
+  // The first weight loads need only the expert; the token rows wait for
+  // the gather indices.
+  load_w(w0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) bsrc[j] = a.A + src_row[j] * a.Kdim + kbeg + kofs;
+  load_b(b0, 0);
+  // Two register stages: the loads of step i+1 are in flight while step i
+  // computes (nsteps is even).
   for (int i = 0; i < nsteps; i += 2) {
-    if (i + 1 < nsteps) load(w1, b1, i + 1);
+    load_w(w1, i + 1);
+    load_b(b1, i + 1);
     compute(w0, b0);
-    if (i + 2 < nsteps) load(w0, b0, i + 2);
-    if (i + 1 < nsteps) compute(w1, b1);
+    load_w(w0, i + 2);
+    load_b(b0, i + 2);
+    compute(w1, b1);
   }
 
-#pragma unroll
-  for (int c = 0; c < 8; ++c)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const f32x4_t v = acc[c][j];
-      red[((wave * 8 + c) * NJ + j) * 64 + lane] = make_float4(v[0], v[1], v[2], v[3]);
-    }
-  __syncthreads();
-
-  // Thread t produces 8 consecutive features (c = 0..7) of one token for
-  // every (j, source lane L, q) -- NJ*256 outputs over 256 threads.
+  // Epilogue, one feature half at a time.  Thread t produces 8 consecutive
+  // features (c = 0..7) of one token for every (j, source lane L, q) --
+  // NJ*256 outputs over the workgroup's threads.
   const float* redf = reinterpret_cast<const float*>(red);
-  for (int o = threadIdx.x; o < NJ * 256; o += 256) {
-    const int L = o & 63;
-    const int q = (o >> 6) & 3;
-    const int j = o >> 8;
-    const int r = row_begin + j * 16 + (L & 15);
-    if (r >= row_end) continue;
-    const int f = f0 + 8 * (4 * (L >> 4) + q);
-    // matrix m is the sum of waves m*kKParts .. m*kKParts + kKParts - 1, in order
-    float sum[M][8];
 #pragma unroll
-    for (int m = 0; m < M; ++m)
+  for (int h = 0; h < 2; ++h) {
+    if (h) __syncthreads();  // the first half's reads are done
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        float t = 0.0f;
+    for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int w = 0; w < C::kKParts; ++w)
-          t += redf[((((m * C::kKParts + w) * 8 + c) * NJ + j) * 64 + L) * 4 + q];
-        sum[m][c] = t;
-      }
-    if (DUAL && a.splits == 1) {
-      uint4 h;
-      h.x = pack_bf16x2(silu_f32(sum[0][0]) * sum[M - 1][0], silu_f32(sum[0][1]) * sum[M - 1][1]);
-      h.y = pack_bf16x2(silu_f32(sum[0][2]) * sum[M - 1][2], silu_f32(sum[0][3]) * sum[M - 1][3]);
-      h.z = pack_bf16x2(silu_f32(sum[0][4]) * sum[M - 1][4], silu_f32(sum[0][5]) * sum[M - 1][5]);
-      h.w = pack_bf16x2(silu_f32(sum[0][6]) * sum[M - 1][6], silu_f32(sum[0][7]) * sum[M - 1][7]);
-      *reinterpret_cast<uint4*>(a.H + (int64_t)r * N + f) = h;
-    } else {
+      for (int j = 0; j < NJ; ++j) red[((wave * 8 + c) * NJ + j) * 64 + lane] = acc[h][c][j];
+    __syncthreads();
+    for (int o = threadIdx.x; o < NJ * 256; o += kThreads) {
+      const int L = o & 63;
+      const int q = (o >> 6) & 3;
+      const int j = o >> 8;
+      const int r = row_begin + j * 16 + (L & 15);
+      if (r >= row_end) continue;
+      const int f = f0 + 128 * h + 8 * (4 * (L >> 4) + q);
+      // matrix m of the workgroup is the sum of waves m*kKParts ..
+      // m*kKParts + kKParts - 1, in order
+      float sum[MW][8];
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        float* dst = a.part + (((int64_t)s * M + m) * a.P + r) * N + f;
-        *reinterpret_cast<float4*>(dst) = make_float4(sum[m][0], sum[m][1], sum[m][2], sum[m][3]);
-        *reinterpret_cast<float4*>(dst + 4) =
-            make_float4(sum[m][4], sum[m][5], sum[m][6], sum[m][7]);
+      for (int m = 0; m < MW; ++m)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          float t = redf[(((m * C::kKParts * 8 + c) * NJ + j) * 64 + L) * 4 + q];
+#pragma unroll
+          for (int w = 1; w < C::kKParts; ++w)
+            t += redf[((((m * C::kKParts + w) * 8 + c) * NJ + j) * 64 + L) * 4 + q];
+          sum[m][c] = t;
+        }
+      if (MODE == kFused) {
+        uint4 hv;
+        hv.x = pack_bf16x2(silu_f32(sum[0][0]) * sum[MW - 1][0], silu_f32(sum[0][1]) * sum[MW - 1][1]);
+        hv.y = pack_bf16x2(silu_f32(sum[0][2]) * sum[MW - 1][2], silu_f32(sum[0][3]) * sum[MW - 1][3]);
+        hv.z = pack_bf16x2(silu_f32(sum[0][4]) * sum[MW - 1][4], silu_f32(sum[0][5]) * sum[MW - 1][5]);
+        hv.w = pack_bf16x2(silu_f32(sum[0][6]) * sum[MW - 1][6], silu_f32(sum[0][7]) * sum[MW - 1][7]);
+        *reinterpret_cast<uint4*>(a.H + (int64_t)r * N + f) = hv;
+      } else {
+#pragma unroll
+        for (int m = 0; m < MW; ++m) {
+          const int slice = s * C::kSlices + (MODE == kPerMatrix ? mat_wg : m);
+          f32x4_t* dst = reinterpret_cast<f32x4_t*>(a.part + ((int64_t)slice * a.P + r) * N + f);
+          __builtin_nontemporal_store(f32x4_t{sum[m][0], sum[m][1], sum[m][2], sum[m][3]}, dst);
+          __builtin_nontemporal_store(f32x4_t{sum[m][4], sum[m][5], sum[m][6], sum[m][7]}, dst + 1);
+        }
       }
     }
   }
@@ -241,22 +341,81 @@ __global__ __launch_bounds__(256) void swiglu_finish_kernel(const float* __restr
   }
 }
 
-template <int NJ, bool DUAL>
+template <int NJ, int MODE>
 hipError_t launch_stream(const StreamArgs& in, hipStream_t stream) {
   StreamArgs a = in;
   a.max_tiles = (int)(((int64_t)a.P + (int64_t)a.E * (16 * NJ - 1)) / (16 * NJ));
   if (a.max_tiles <= 0) return hipSuccess;
-  const int64_t grid = (int64_t)a.max_tiles * a.splits * (a.N / kFeat);
-  hipLaunchKernelGGL((stream_gemm_kernel<NJ, DUAL>), dim3((unsigned)grid), dim3(256), 0, stream,
-                     a);
+  const int64_t grid =
+      (int64_t)a.max_tiles * a.splits * (a.N / kFeat) * (MODE == kPerMatrix ? 2 : 1);
+  hipLaunchKernelGGL((stream_gemm_kernel<NJ, MODE>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool stream_gemm_supported(int Kdim, int N, int splits) {
-  // one matrix: the k-range of a split is cut in four, two matrices: in two
-  return splits >= 1 && N % kFeat == 0 && Kdim % (splits * kWaves * 32) == 0;
+namespace {
+
+// A launch whose workgroups put `kparts` waves on one matrix, K split
+// `splits` ways: every wave takes an even number of k-steps of 32 (and, when
+// K is split, at least four), and a k-step's 32 weight rows stay under 2 GiB
+// (32-bit buffer offsets).
+bool stream_shape_ok(int Kdim, int N, int kparts, int splits) {
+  return splits >= 1 && N % kFeat == 0 && Kdim % (splits * kparts * 64) == 0 &&
+         (splits == 1 || Kdim / (splits * kparts) >= 128) &&
+         (int64_t)32 * N * 2 < (int64_t(1) << 31);
+}
+
+// Picks among candidate launches, given as busy-workgroup counts in
+// increasing order (index 0 = the unsplit launch):
+//   * the largest candidate that is one round of workgroups (one per compute
+//     unit) filling at least 55 % of the compute units;
+//   * else the unsplit launch when it alone makes at least 1.7 rounds (no
+//     partial sums at all);
+//   * else the smallest candidate with at least 3 rounds (the largest if
+//     none has).
+int pick_launch(const double* wgs, int n) {
+  int one = -1;
+  for (int i = 0; i < n; ++i)
+    if (wgs[i] <= kComputeUnits && wgs[i] >= 0.55 * kComputeUnits) one = i;
+  if (one >= 0) return one;
+  if (wgs[0] >= 1.7 * kComputeUnits) return 0;
+  for (int i = 0; i < n; ++i)
+    if (wgs[i] >= 3.0 * kComputeUnits) return i;
+  return n - 1;
+}
+
+}  // namespace
+
+int stream_swiglu_splits(int d, int d_ff, double tiles) {
+  if (!stream_shape_ok(d, d_ff, kWaves / 2, 1)) return -1;
+  const double per = tiles * (d_ff / kFeat);  // busy workgroups of the fused launch
+  double wgs[16];
+  int split[16];
+  int n = 0;
+  wgs[n] = per;
+  split[n++] = 0;
+  for (int s = 1; s <= 64 && n < 16; ++s)
+    if (stream_shape_ok(d, d_ff, kWaves, s)) {
+      wgs[n] = 2.0 * s * per;
+      split[n++] = s;
+    }
+  return split[pick_launch(wgs, n)];
+}
+
+int stream_down_splits(int d_ff, int d, double tiles) {
+  if (!stream_shape_ok(d_ff, d, kWaves, 1)) return 0;
+  const double per = tiles * (d / kFeat);
+  double wgs[16];
+  int split[16];
+  int n = 0;
+  for (int s = 1; s <= 64 && n < 16; ++s)
+    if (stream_shape_ok(d_ff, d, kWaves, s)) {
+      wgs[n] = s * per;
+      split[n++] = s;
+    }
+  return split[pick_launch(wgs, n)];
 }
 
 hipError_t launch_stream_swiglu_bf16(const void* x, const int32_t* sorted_token,
@@ -276,7 +435,11 @@ hipError_t launch_stream_swiglu_bf16(const void* x, const int32_t* sorted_token,
   a.E = E;
   a.P = P;
   a.splits = splits;
-  return launch_stream<1, true>(a, stream);
+  if (splits == 0) {
+    a.splits = 1;
+    return launch_stream<1, kFused>(a, stream);
+  }
+  return launch_stream<1, kPerMatrix>(a, stream);
 }
 
 hipError_t launch_swiglu_finish_bf16(const float* part, int splits, int P, int d_ff, void* H,
@@ -305,7 +468,7 @@ hipError_t launch_stream_down_bf16(const void* H, const ExpertPtrs& W2, const in
   a.E = E;
   a.P = P;
   a.splits = splits;
-  return launch_stream<1, false>(a, stream);
+  return launch_stream<1, kDown>(a, stream);
 }
 
 }  // namespace moe

@@ -1,6 +1,7 @@
 // C ABI of the MoE layer forward: host-side validation, workspace carving and
 // the launch sequence.  Declarations and contracts: include/moe_mi355x.h.
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <atomic>
 #include <cstdio>
@@ -67,24 +68,11 @@ moe_status check_shape(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K,
 }
 
 struct Plan {
-  int swiglu_splits = 1;
+  int swiglu_splits = 0;
   int down_splits = 1;
   size_t scratch = 0;
   bool streaming = false;
 };
-
-// Smallest K split that gives the grid at least ~8 workgroups per compute
-// unit, keeping >= 4 k-steps of 32 per wavefront.
-int choose_splits(int64_t Kdim, int64_t base_blocks) {
-  int best = 1;
-  for (int s = 1; s <= 64; ++s) {
-    if (!moe::stream_gemm_supported((int)Kdim, 128, s)) continue;
-    if (Kdim / (s * 4) < 128) break;
-    best = s;
-    if (base_blocks * s >= 2048) break;
-  }
-  return best;
-}
 
 // Batches whose expert segments fit one 16-row token tile per expert in the
 // common case (T*K <= 64) stream the weights; larger ones use the tiled
@@ -102,14 +90,19 @@ Plan make_plan(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K, int32_t
     }
     return p;
   }
-  if (!moe::stream_gemm_supported((int)d, (int)d_ff, 1) ||
-      !moe::stream_gemm_supported((int)d_ff, (int)d, 1))
-    return p;
+  // The split count is sized for the token tiles expected to hold rows: the
+  // expected number of distinct experts among T tokens choosing K of E
+  // uniformly, E (1 - (1 - K/E)^T), at least P/16, at most the worst case.
+  const double busy = E * (1.0 - std::pow(1.0 - (double)K / E, (double)T));
+  const double tiles = std::min<double>(std::max<double>(busy, P / 16.0),
+                                        (double)((P + (int64_t)E * 15) / 16));
+  const int s1 = moe::stream_swiglu_splits((int)d, (int)d_ff, tiles);
+  const int s2 = moe::stream_down_splits((int)d_ff, (int)d, tiles);
+  if (s1 < 0 || s2 == 0) return p;
   p.streaming = true;
-  const int64_t max_tiles = (P + (int64_t)E * 15) / 16;
-  p.swiglu_splits = choose_splits(d, max_tiles * (d_ff / 128));
-  p.down_splits = choose_splits(d_ff, max_tiles * (d / 128));
-  if (p.swiglu_splits > 1) p.scratch = (size_t)p.swiglu_splits * 2 * P * d_ff * sizeof(float);
+  p.swiglu_splits = s1;
+  p.down_splits = s2;
+  if (p.swiglu_splits > 0) p.scratch = (size_t)p.swiglu_splits * 2 * P * d_ff * sizeof(float);
   return p;
 }
 
@@ -313,7 +306,7 @@ moe_status moe_swiglu_finish(const void* scratch, int64_t T, int64_t d, int64_t 
   moe_status s = check_shape(T, d, d_ff, E, K, dtype);
   if (s) return s;
   const Plan plan = make_plan(T, d, d_ff, E, K, dtype);
-  if (T == 0 || plan.swiglu_splits == 1) return ok();
+  if (T == 0 || plan.swiglu_splits == 0) return ok();
   if (!scratch || !H) return fail(MOE_EINVAL, "NULL pointer");
   if (!aligned16(scratch) || !aligned16(H))
     return fail(MOE_EUNSUPPORTED, "scratch and H must be 16-byte aligned");
@@ -425,7 +418,7 @@ moe_status moe_forward(const void* x, const void* W_g, const void* const* W1,
   e = run_swiglu(plan, x, sorted_token, p1, p3, offsets, P, (int)d, (int)d_ff, E, dtype, H,
                  scratch, st);
   if (e != hipSuccess) return hip_status(e, "expert_swiglu");
-  if (plan.swiglu_splits > 1) {
+  if (plan.swiglu_splits > 0) {
     e = moe::launch_swiglu_finish_bf16(static_cast<const float*>(scratch), plan.swiglu_splits, P,
                                        (int)d_ff, H, st);
     if (e != hipSuccess) return hip_status(e, "swiglu_finish");

@@ -37,8 +37,16 @@ hipError_t launch_expert_down_f32(const void* H, const ExpertPtrs& W2, const int
                                   int P, int d, int d_ff, int E, float* O, hipStream_t stream);
 
 // Weight-streaming variants for small batches (every expert segment of at
-// most 16 rows per token tile); K split over `splits` workgroups.
-bool stream_gemm_supported(int Kdim, int N, int splits);
+// most 16 rows per token tile), N in tiles of kStreamFeat features.
+constexpr int kStreamFeat = 256;
+// W1/W3 launch when about `tiles` token tiles hold rows: 0 = fused (H written
+// by the product), s >= 1 = one matrix per workgroup with K split s ways
+// (fp32 partial sums, completed by launch_swiglu_finish_bf16); -1 if the
+// shape cannot stream.
+int stream_swiglu_splits(int d, int d_ff, double tiles);
+// W2 K split (slices of O) for about `tiles` busy token tiles; 0 if the
+// shape cannot stream.
+int stream_down_splits(int d_ff, int d, double tiles);
 hipError_t launch_stream_swiglu_bf16(const void* x, const int32_t* sorted_token,
                                      const ExpertPtrs& W1, const ExpertPtrs& W3,
                                      const int32_t* offsets, int P, int d, int d_ff, int E,

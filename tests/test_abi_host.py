@@ -48,17 +48,19 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     assert lib.moe_status_str(0) == b"MOE_OK"
     assert lib.moe_status_str(4) == b"MOE_EHIP"
 
 
 def test_plan(lib):
     p = M.plan_for(8, 4096, 14336, 8, 2, M.BF16)
-    assert p["streaming"] and p["swiglu_splits"] > 1 and p["down_splits"] > 1
+    assert p["streaming"] and p["swiglu_splits"] >= 1 and p["down_splits"] > 1
     assert p["swiglu_scratch_bytes"] == p["swiglu_splits"] * 2 * 16 * 14336 * 4
+    p = M.plan_for(32, 4096, 14336, 8, 2, M.BF16)     # fused W1/W3: H written directly
+    assert p["streaming"] and p["swiglu_splits"] == 0 and p["swiglu_scratch_bytes"] == 0
     p = M.plan_for(4096, 4096, 14336, 8, 2, M.BF16)
-    assert not p["streaming"] and p["swiglu_splits"] == 1 and p["swiglu_scratch_bytes"] == 0
+    assert not p["streaming"] and p["swiglu_splits"] == 0 and p["swiglu_scratch_bytes"] == 0
     assert p["down_splits"] >= 1 and 14336 % (128 * p["down_splits"]) == 0
     p = M.plan_for(8, 128, 256, 8, 2, M.F32)
     assert not p["streaming"]

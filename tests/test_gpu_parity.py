@@ -204,7 +204,8 @@ def test_layer_bf16_small(dev, T, d, d_ff):
 
 
 @pytest.mark.parametrize("T,d,d_ff", [(8, 2048, 1024), (3, 1024, 2048), (32, 512, 1536),
-                                      (8, 1024, 512), (1, 1024, 1024)])
+                                      (8, 1024, 512), (1, 1024, 1024), (5, 1024, 2560),
+                                      (16, 768, 2048)])
 def test_layer_bf16_streaming_splits(dev, T, d, d_ff):
     """Small batches take the weight-streaming kernels with K split over
     workgroups (partial sums added in split order)."""
@@ -295,7 +296,8 @@ def test_rmsnorm(dev, dtype):
 
 # ---------------------------------------------------------------- full size
 def _full(name, dev, tokens, check_perm_all=True):
-    w = W.WORKLOADS[name]
+    w = W.WORKLOADS[name] if isinstance(name, str) else name
+    name = w.name
     say("full size", name)
     inp = W.layer_inputs(w, dev)
     y32, v = run_forward(inp, w.K)
@@ -322,6 +324,18 @@ def _full(name, dev, tokens, check_perm_all=True):
 
 def test_full_decode_T8(dev):
     _full("decode_bf16_T8", dev, tokens=range(8))
+
+
+@pytest.mark.parametrize("T", [1, 2, 4])
+def test_full_decode_small_batches(dev, T):
+    """Mixtral shape at 1, 2 and 4 tokens: the streaming plan takes the
+    per-matrix W1/W3 form with 1 and 2 K splits and the fused form, and
+    splits W2 7, 4 and 2 ways."""
+    w = W.scaled(W.WORKLOADS["decode_bf16_T8"], name="decode_bf16_T%d" % T, T=T)
+    plan = M.plan_for(w.T, w.d, w.d_ff, w.E, w.K, M.BF16)
+    say("full decode", T, plan)
+    assert plan["streaming"]
+    _full(w, dev, tokens=range(T))
 
 
 def test_full_T512_sampled(dev):
