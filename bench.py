@@ -130,8 +130,10 @@ def time_layer(layer: Layer, steps: int, warmup: int):
     current stream, no host synchronisation inside): `steps` of them between
     two synchronisations.  A second pass runs the same kernels through the
     stage entry points with HIP events between them, for per-kernel times.
-    Returns (wall seconds of the moe_forward steps, per-stage mean ms, wall
-    seconds of the staged steps)."""
+    Returns (wall seconds of the moe_forward steps, per-stage median ms, wall
+    seconds of the staged steps).  Medians: an event pair also times any
+    idle gap while the host is late with the next launch, and one such
+    stall would dominate a mean."""
     for _ in range(warmup):
         layer.forward_call()
     torch.cuda.synchronize()
@@ -152,7 +154,7 @@ def time_layer(layer: Layer, steps: int, warmup: int):
         layer.step(evs[i])
     torch.cuda.synchronize()
     wall_staged = time.perf_counter() - t1
-    per_stage = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
+    per_stage = {name: float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs]))
                  for j, name in enumerate(STAGES)}
     return wall_fwd, per_stage, wall_staged
 
@@ -164,7 +166,7 @@ def time_cold(layer: Layer, steps: int):
     """Each step timed alone with HIP events after writing a 1 GiB buffer, so
     neither L2 nor the 256 MB Infinity Cache holds a tail of the weights from
     the previous step: moe_forward steps (percentiles of the whole call), then
-    staged steps (per-stage means, for the kernel roofline)."""
+    staged steps (per-stage medians, for the kernel roofline)."""
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=layer.x.device)
     tot = []
     for i in range(steps):
@@ -190,7 +192,7 @@ def time_cold(layer: Layer, steps: int):
                 ms_p10=round(float(np.percentile(tot, 10)), 4),
                 ms_p90=round(float(np.percentile(tot, 90)), 4),
                 staged_ms_median=round(float(np.median(per.sum(axis=1))), 4),
-                stage_ms={name: round(float(per[:, j].mean()), 4) for j, name in enumerate(STAGES)})
+                stage_ms={name: round(float(np.median(per[:, j])), 4) for j, name in enumerate(STAGES)})
 
 
 # The W1/W3 stage is one launch of the kernel below (the split finish is a
@@ -198,15 +200,23 @@ def time_cold(layer: Layer, steps: int):
 # summary, keyed by kernel, workload and the sha256 of the kernel's source.
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.txt")
 CSRC = os.path.join(ROOT, "sparse_mixture_experts_32_amd", "csrc")
-SWIGLU_KERNEL = {True: ("stream_gemm_kernel<1, true>", "expert_stream_bf16.hip"),
-                 False: ("tiled_gemm_kernel<256, true>", "expert_tiled_bf16.hip")}
 
 
-def measured_traffic(workload, streaming):
+def swiglu_kernel(plan):
+    """(kernel name as the profiler prints it, source file) of the W1/W3
+    stage: the streaming kernel in its fused (1) or per-matrix (2) form, or
+    the tiled kernel."""
+    if plan["streaming"]:
+        form = 1 if plan["swiglu_splits"] == 0 else 2
+        return "stream_gemm_kernel<1, %d>" % form, "expert_stream_bf16.hip"
+    return "tiled_gemm_kernel<256, true>", "expert_tiled_bf16.hip"
+
+
+def measured_traffic(workload, plan):
     """Calibrated FETCH+WRITE bytes per dispatch of the W1/W3 kernel, or None
     when no row matches this workload or the kernel source changed since the
     counters were taken."""
-    kernel, src = SWIGLU_KERNEL[bool(streaming)]
+    kernel, src = swiglu_kernel(plan)
     try:
         import hashlib
         sha = hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest()
@@ -220,11 +230,11 @@ def measured_traffic(workload, streaming):
     return None
 
 
-def roofline_for(w, alg, per_stage_ms, streaming):
+def roofline_for(w, alg, per_stage_ms, plan):
     g1_ms = per_stage_ms["expert_swiglu"]
     intensity = alg["swiglu_flops"] / alg["swiglu_bytes"]
-    kernel = SWIGLU_KERNEL[bool(streaming)][0]
-    traffic = measured_traffic(w.name, streaming)
+    kernel = swiglu_kernel(plan)[0]
+    traffic = measured_traffic(w.name, plan)
     if intensity < 312:
         achieved = alg["swiglu_bytes"] / (g1_ms * 1e-3) / 1e9
         return dict(kernel=kernel, bound="hbm", achieved=round(achieved, 1),
@@ -283,9 +293,9 @@ def run_workload(name, dev, steps, warmup):
                layer_roofline_frac=round(max(alg["layer_bytes"] / (HBM_PEAK_GBS * 1e9),
                                              alg["layer_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12))
                                          / (ms * 1e-3), 4),
-               roofline=roofline_for(w, alg, per_stage, layer.plan["streaming"]))
+               roofline=roofline_for(w, alg, per_stage, layer.plan))
     cold = time_cold(layer, steps)
-    cold["roofline"] = roofline_for(w, alg, cold["stage_ms"], layer.plan["streaming"])
+    cold["roofline"] = roofline_for(w, alg, cold["stage_ms"], layer.plan)
     res["cold_cache"] = cold
     return res, layer
 
