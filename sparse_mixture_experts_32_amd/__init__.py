@@ -250,9 +250,10 @@ def moe_route_permute(topk_idx, E, offsets=None, sorted_token=None, pos=None, st
 
 def moe_expert_swiglu(x, W1, W3, K, offsets, sorted_token, H=None, scratch=None, stream=None,
                       finish=True):
-    """H for every expert-sorted row.  With a K-split plan (small batches)
-    the partial sums land in ``scratch`` and, when ``finish`` is true,
-    moe_swiglu_finish completes H (pass finish=False to launch it yourself)."""
+    """H for every expert-sorted row.  When the plan's W1/W3 product leaves
+    partial sums (plan_for(...)["swiglu_splits"] > 0, small batches) they land
+    in ``scratch`` and, when ``finish`` is true, moe_swiglu_finish completes H
+    (pass finish=False to launch it yourself)."""
     lib = load_library()
     T, d = x.shape
     E = len(W1)
