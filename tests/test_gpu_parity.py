@@ -229,6 +229,18 @@ def test_layer_bf16_k_and_e(dev, E, K):
     check_layer(W.layer_inputs(w, dev), K)
 
 
+# decode-sized batches with many experts take the streaming kernels: most
+# experts hold no rows, and the worst-case grid has a token tile per expert
+@pytest.mark.parametrize("T,d,d_ff,E,K", [(8, 512, 1024, 16, 3), (16, 512, 512, 64, 4),
+                                          (5, 1024, 512, 64, 4), (21, 256, 1024, 16, 3)])
+def test_layer_bf16_streaming_many_experts(dev, T, d, d_ff, E, K):
+    w = small(T=T, d=d, d_ff=d_ff, E=E, K=K)
+    plan = M.plan_for(T, d, d_ff, E, K, M.BF16)
+    say("layer streaming E K", T, E, K, plan)
+    assert plan["streaming"]
+    check_layer(W.layer_inputs(w, dev), K)
+
+
 def test_layer_f32_general_sizes(dev):
     w = small(T=77, d=96, d_ff=200, dtype="f32")
     say("layer f32 ragged", w.T, w.d, w.d_ff)
