@@ -229,11 +229,15 @@ def test_layer_bf16_k_and_e(dev, E, K):
     check_layer(W.layer_inputs(w, dev), K)
 
 
-# decode-sized batches with many experts take the streaming kernels: most
-# experts hold no rows, and the worst-case grid has a token tile per expert
+# decode-sized batches take the streaming kernels with any number of
+# experts: with many, most experts hold no rows and the worst-case grid has a
+# token tile per expert; with one or two, an expert's rows span several
+# 16-row token tiles, each streaming the expert's weights
 @pytest.mark.parametrize("T,d,d_ff,E,K", [(8, 512, 1024, 16, 3), (16, 512, 512, 64, 4),
-                                          (5, 1024, 512, 64, 4), (21, 256, 1024, 16, 3)])
-def test_layer_bf16_streaming_many_experts(dev, T, d, d_ff, E, K):
+                                          (5, 1024, 512, 64, 4), (21, 256, 1024, 16, 3),
+                                          (40, 512, 1024, 1, 1), (32, 512, 512, 2, 2),
+                                          (64, 256, 512, 1, 1)])
+def test_layer_bf16_streaming_experts(dev, T, d, d_ff, E, K):
     w = small(T=T, d=d, d_ff=d_ff, E=E, K=K)
     plan = M.plan_for(T, d, d_ff, E, K, M.BF16)
     say("layer streaming E K", T, E, K, plan)
