@@ -265,14 +265,71 @@ def cpu_baseline(layer: Layer, max_tokens: int = 8):
     W2 = [t.float().cpu().numpy() for t in layer.W2]
     reps, t0 = 0, time.perf_counter()
     while True:        # repeat the sample until ~10 s of CPU work (at least 3 runs)
-        O.moe_forward(x, Wg, W1, W3, W2, w.K, faithful=True)
+        y_ref, aux = O.moe_forward(x, Wg, W1, W3, W2, w.K, faithful=True)
         reps += 1
         if reps >= 3 and time.perf_counter() - t0 >= 10.0:
             break
     dt = (time.perf_counter() - t0) / reps
-    return dict(value=round(n / dt, 3), unit="tokens/s", cores=int(threads), kind="oracle",
+    base = dict(value=round(n / dt, 3), unit="tokens/s", cores=int(threads), kind="oracle",
+                cpu_model=cpu_model(),
                 sample="first %d of %d tokens of %s, float64 oracle in faithful mode, "
                        "%.2f s per run, mean of %d runs" % (n, w.T, w.name, dt, reps))
+    return base, parity_against(layer, n, y_ref, aux)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def parity_against(layer: Layer, n, y_ref, aux):
+    """The layer's GPU outputs for its first n tokens against the oracle
+    output the CPU leg computed: routing of decided tokens (fp64 margin
+    between the K-th and (K+1)-th logit above 1e-3), gate weights, the fp32
+    output's max error over rms, and the bf16 store = RNE(fp32 output)."""
+    w = layer.w
+    K = w.K
+    ws = torch.empty(M.workspace_size(w.T, w.d, w.d_ff, w.E, K, M.BF16), dtype=torch.uint8,
+                     device=layer.x.device)
+    y32 = M.moe_forward(layer.x, layer.W_g, layer.W1, layer.W3, layer.W2, K,
+                        y_dtype=torch.float32, workspace=ws)
+    views = M.workspace_views(ws, w.T, w.d, w.d_ff, w.E, K, M.BF16)
+    yb = M.moe_forward(layer.x, layer.W_g, layer.W1, layer.W3, layer.W2, K)
+    torch.cuda.synchronize()
+    gi = views["topk_idx"][:n].cpu().numpy()
+    gw = views["topk_w"][:n].cpu().numpy()
+    srt = -np.sort(-aux["logits"], axis=1)
+    decided = srt[:, K - 1] - srt[:, K] > 1e-3 if K < w.E else np.ones(n, dtype=bool)
+    ordered = decided & np.all(srt[:, :K - 1] - srt[:, 1:K] > 1e-3, axis=1)
+    set_ok = np.array([sorted(gi[t]) == sorted(aux["idx"][t]) for t in range(n)])
+    rank_ok = np.all(gi == aux["idx"], axis=1)
+    y = y32[:n].double().cpu().numpy()
+    rows = decided & set_ok
+    err = (float(np.abs(y[rows] - y_ref[rows]).max() / np.sqrt(np.mean(y_ref[rows] ** 2)))
+           if rows.any() else None)
+    return dict(tokens=int(n), decided=int(decided.sum()),
+                expert_set_mismatches=int(np.sum(decided & ~set_ok)),
+                rank_order_mismatches=int(np.sum(ordered & ~rank_ok)),
+                max_gate_weight_err=float(np.abs(gw - aux["w"])[ordered & rank_ok].max())
+                if np.any(ordered & rank_ok) else None,
+                rel_err_faithful=err, tol=1e-2,
+                bf16_store_is_rne_of_fp32=bool(torch.equal(yb, y32.to(torch.bfloat16))))
+
+
+def input_record(w, layer):
+    """The workload's seed and the SHA-256 of the token and router bytes the
+    GPU consumed (the expert weights come from per-tensor seeds derived from
+    the same seed)."""
+    import hashlib
+
+    def sha(t):
+        return hashlib.sha256(t.contiguous().view(torch.uint8).cpu().numpy().tobytes()).hexdigest()
+    return dict(seed=w.seed, x_sha256=sha(layer.x), W_g_sha256=sha(layer.W_g))
 
 
 def run_workload(name, dev, steps, warmup):
@@ -285,6 +342,7 @@ def run_workload(name, dev, steps, warmup):
     alg = algorithmic(w, counts)
     ms = wall / steps * 1e3
     res = dict(workload=name, T=w.T, steps=steps, ms_per_step=round(ms, 4),
+               inputs=input_record(w, layer),
                tokens_per_s=round(w.T * steps / wall, 1),
                ms_per_step_staged=round(wall_staged / steps * 1e3, 4),
                stage_ms={k: round(v, 4) for k, v in per_stage.items()},
@@ -537,7 +595,7 @@ def main():
     head, layer = run_workload(HEADLINE, dev, args.steps, args.warmup)
     print("# %s done: %.3f ms/step" % (HEADLINE, head["ms_per_step"]), file=sys.stderr,
           flush=True)
-    cpu = None if args.no_cpu else cpu_baseline(layer)
+    cpu, parity = (None, None) if args.no_cpu else cpu_baseline(layer)
     del layer
     torch.cuda.empty_cache()
     sweep = []
@@ -577,6 +635,7 @@ def main():
                    "experts": w.E, "top_k": w.K, "parallelism": "single GPU"},
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
+        "parity": parity,
         "detail": {k: v for k, v in head.items() if k not in ("roofline",)},
         "sweep": sweep,
         "decode_sweep": decode_sweep,
