@@ -494,6 +494,36 @@ def _time_stack(h, h0, run, steps, warmup):
     return t
 
 
+def run_dense_reference(dev, steps=10, warmup=3):
+    """Context, not the product: torch.matmul (hipBLASLt) on the dense
+    equivalents of the prefill products -- all 8192 (token, expert) rows
+    against one [4096, 28672] W1|W3 matrix and one [14336, 4096] W2 matrix,
+    bf16 with fp32 accumulation, contiguous row-major operands -- timed
+    with HIP events."""
+    g = torch.Generator(device=dev).manual_seed(7)
+    out = []
+    for name, m, k, n in [("w1w3_dense", 8192, 4096, 2 * 14336), ("w2_dense", 8192, 14336, 4096)]:
+        a = torch.randn((m, k), generator=g, device=dev).to(torch.bfloat16)
+        b = (torch.randn((k, n), generator=g, device=dev) / k ** 0.5).to(torch.bfloat16)
+        for _ in range(warmup):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tflops = 2.0 * m * k * n / (ms * 1e-3) / 1e12
+        out.append(dict(product=name, shape=[m, k, n], ms=round(ms, 4),
+                        tflops=round(tflops, 1), mfma_frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)))
+        del a, b
+        torch.cuda.empty_cache()
+    return out
+
+
 def run_stacks(dev, steps, warmup, decode_steps):
     """The 32-block stack (RMSNorm + MoE + residual per block, 90 GB of
     expert weights resident): T = 4096 tokens per step, and the same blocks
@@ -614,6 +644,10 @@ def main():
         print("# %s done: %.4f ms/call" % (r["workload"], r["ms_per_call"]), file=sys.stderr,
               flush=True)
     stack = None if (args.no_sweep or args.no_stack) else run_stacks(dev, 3, 1, 10)
+    dense = None if args.no_sweep else run_dense_reference(dev)
+    for r in dense or []:
+        print("# dense %s (torch.matmul) done: %.3f ms" % (r["product"], r["ms"]), file=sys.stderr,
+              flush=True)
     for r in stack or []:
         print("# %s done: %.1f ms/step" % (r["workload"], r["ms_per_step"]), file=sys.stderr,
               flush=True)
@@ -640,6 +674,7 @@ def main():
         "sweep": sweep,
         "decode_sweep": decode_sweep,
         "stack": stack,
+        "dense_reference": dense,
         "attention": attention,
     }
     print(json.dumps(out), flush=True)
