@@ -163,14 +163,17 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const T* __restrict__ 
     for (int r = 0; r < K; ++r) out_w[r] = out_w[r] / denom;
 }
 
-// Many tokens, 8 experts, bf16: each wavefront takes 4 tokens, so every
+// Many tokens, 8 experts, bf16: a workgroup takes 4 tokens, so every
 // 16-byte piece of W_g it loads serves 4 tokens (a token per wavefront would
-// read all of W_g once per token).  Lane l accumulates the 8-wide feature
-// chunks l, l + 64, ... of each token; after the transposed butterfly lane
-// l holds expert l / 8 of each token.  Top-K then runs for the 4 tokens at
-// once: lane 16 n + e (e < 8) holds expert e of token n, and K rounds of an
-// arg-max over each 16-lane group pick the experts with key (-logit, index),
-// as in the general kernel.
+// read all of W_g once per token), and its 4 wavefronts split the features:
+// lane l of wave w accumulates the 8-wide chunks 64 w + l, 64 w + l + 256,
+// ... of each token.  (One wavefront per 4 tokens left one wave per SIMD
+// at T = 4096 and ran 3x longer: every load round trip was exposed.)  After
+// the transposed butterfly lane l holds expert l / 8 of the wave's partial;
+// the 4 partials are added in wave order through LDS.  Top-K then runs for
+// the 4 tokens at once in wave 0: lane 16 n + e (e < 8) holds expert e of
+// token n, and K rounds of an arg-max over each 16-lane group pick the
+// experts with key (-logit, index), as in the general kernel.
 constexpr int kRouterTokPerWave = 4;
 
 __global__ __launch_bounds__(256) void router_e8_kernel(const bf16_t* __restrict__ x,
@@ -180,10 +183,11 @@ __global__ __launch_bounds__(256) void router_e8_kernel(const bf16_t* __restrict
                                                         float* __restrict__ topk_w,
                                                         float* __restrict__ logits_out) {
   constexpr int NT = kRouterTokPerWave;
+  __shared__ float part[4][NT][8];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int t0 = (blockIdx.x * 4 + wave) * NT;         // first token of this wavefront
-  if (t0 >= T_) return;                                 // wave-uniform; no barriers below
+  const int t0 = blockIdx.x * NT;                       // first token of this workgroup
+  if (t0 >= T_) return;                                 // workgroup-uniform
   const bf16_t* xr[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) xr[n] = x + (int64_t)min(t0 + n, T_ - 1) * d;
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(256) void router_e8_kernel(const bf16_t* __restrict
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[n][j] = 0.0f;
 #pragma unroll 2
-  for (int k0 = lane * 8; k0 < d; k0 += 64 * 8) {
+  for (int k0 = (wave * 64 + lane) * 8; k0 < d; k0 += 256 * 8) {
     float wv[8][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -208,9 +212,19 @@ __global__ __launch_bounds__(256) void router_e8_kernel(const bf16_t* __restrict
         for (int j = 0; j < 8; ++j) acc[n][j] = fmaf(xv[i], wv[i][j], acc[n][j]);
     }
   }
-  float lg[NT];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) lg[n] = wave_sum8(acc[n], lane);   // expert lane / 8
+  for (int n = 0; n < NT; ++n) {
+    const float s = wave_sum8(acc[n], lane);              // expert lane / 8
+    if ((lane & 7) == 0) part[wave][n][lane >> 3] = s;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float lg[NT];                                         // lane l: expert l / 8 of token n
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int e = lane >> 3;
+    lg[n] = ((part[0][n][e] + part[1][n][e]) + part[2][n][e]) + part[3][n][e];
+  }
   if (logits_out && (lane & 7) == 0) {
 #pragma unroll
     for (int n = 0; n < NT; ++n)
@@ -274,7 +288,7 @@ hipError_t launch_router_topk(const void* x, const void* Wg, int T, int d, int E
                    (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(Wg) & 15) == 0;
   if (dtype == kBF16 && vec && !wide && E == 8 && K <= 8) {
-    const int per_block = 4 * kRouterTokPerWave;
+    const int per_block = kRouterTokPerWave;
     hipLaunchKernelGGL(router_e8_kernel, dim3((T + per_block - 1) / per_block), dim3(256), 0,
                        stream, static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(Wg), T, d,
                        K, topk_idx, topk_w, logits);

@@ -99,15 +99,17 @@ def check_layer(inp, K, tokens=None, bf16_store=True):
 
 
 # ---------------------------------------------------------------- router
-# T >= 1024 with 8 experts takes the many-token router (4 tokens per wavefront),
-# fewer tokens the general one; the small batches cover decode sizes and a
-# d (6144) whose k-loop runs a ragged number of chunks per thread
+# T >= 1024 with 8 experts takes the many-token router (4 tokens per workgroup,
+# the features split over its 4 wavefronts), fewer tokens the general one; the
+# small batches cover decode sizes, and d = 6144 gives k-loops with a ragged
+# number of chunks per thread (and per wavefront in the many-token router)
 @pytest.mark.parametrize("dtype,T,K,d", [("bf16", 300, 2, 256), ("f32", 300, 2, 256),
                                          ("bf16", 1500, 2, 256), ("bf16", 1027, 1, 256),
                                          ("bf16", 1100, 4, 256), ("f32", 1100, 2, 256),
                                          ("bf16", 1, 2, 256), ("bf16", 8, 8, 256),
                                          ("bf16", 13, 4, 512), ("bf16", 32, 2, 6144),
-                                         ("bf16", 21, 3, 4096), ("f32", 8, 2, 256)])
+                                         ("bf16", 21, 3, 4096), ("f32", 8, 2, 256),
+                                         ("bf16", 1030, 2, 6144), ("bf16", 1024, 2, 4096)])
 def test_router_small(dev, dtype, T, K, d):
     w = small(T=T, d=d, d_ff=128, dtype=dtype)
     say("router", dtype, w.T, w.d, K)
