@@ -495,30 +495,42 @@ def _time_stack(h, h0, run, steps, warmup):
 
 
 def run_dense_reference(dev, steps=10, warmup=3):
-    """Context, not the product: torch.matmul (hipBLASLt) on the dense
-    equivalents of the prefill products -- all 8192 (token, expert) rows
-    against one [4096, 28672] W1|W3 matrix and one [14336, 4096] W2 matrix,
-    bf16 with fp32 accumulation, contiguous row-major operands -- timed
-    with HIP events."""
+    """Context, not the product: hipBLASLt through torch on dense stand-ins
+    for the products, bf16 with fp32 accumulation, contiguous row-major
+    operands, timed with HIP events.  Prefill: all 8192 (token, expert) rows
+    against one [4096, 28672] W1|W3 matrix and one [14336, 4096] W2 matrix
+    (torch.matmul).  T = 512: eight equal groups of 128 rows, one per
+    expert, each against its own weights (torch.bmm over [8, ...] stacks:
+    the same 1.88 GB and 0.94 GB of weights as the layer reads), reported
+    also as weight bytes per second."""
     g = torch.Generator(device=dev).manual_seed(7)
     out = []
-    for name, m, k, n in [("w1w3_dense", 8192, 4096, 2 * 14336), ("w2_dense", 8192, 14336, 4096)]:
-        a = torch.randn((m, k), generator=g, device=dev).to(torch.bfloat16)
-        b = (torch.randn((k, n), generator=g, device=dev) / k ** 0.5).to(torch.bfloat16)
+    for name, bsz, m, k, n in [("w1w3_dense", 1, 8192, 4096, 2 * 14336),
+                               ("w2_dense", 1, 8192, 14336, 4096),
+                               ("w1w3_8x128_batched", 8, 128, 4096, 2 * 14336),
+                               ("w2_8x128_batched", 8, 128, 14336, 4096)]:
+        shape_a = (m, k) if bsz == 1 else (bsz, m, k)
+        shape_b = (k, n) if bsz == 1 else (bsz, k, n)
+        a = torch.randn(shape_a, generator=g, device=dev).to(torch.bfloat16)
+        b = (torch.randn(shape_b, generator=g, device=dev) / k ** 0.5).to(torch.bfloat16).contiguous()
+        prod = torch.matmul if bsz == 1 else torch.bmm
         for _ in range(warmup):
-            torch.matmul(a, b)
+            prod(a, b)
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(steps):
-            torch.matmul(a, b)
+            prod(a, b)
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / steps
-        tflops = 2.0 * m * k * n / (ms * 1e-3) / 1e12
-        out.append(dict(product=name, shape=[m, k, n], ms=round(ms, 4),
-                        tflops=round(tflops, 1), mfma_frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)))
+        tflops = 2.0 * bsz * m * k * n / (ms * 1e-3) / 1e12
+        res = dict(product=name, shape=[bsz, m, k, n] if bsz > 1 else [m, k, n], ms=round(ms, 4),
+                   tflops=round(tflops, 1), mfma_frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4))
+        if bsz > 1:
+            res["weight_gbps"] = round(bsz * k * n * 2 / (ms * 1e-3) / 1e9, 1)
+        out.append(res)
         del a, b
         torch.cuda.empty_cache()
     return out
