@@ -658,7 +658,7 @@ def main():
     stack = None if (args.no_sweep or args.no_stack) else run_stacks(dev, 3, 1, 10)
     dense = None if args.no_sweep else run_dense_reference(dev)
     for r in dense or []:
-        print("# dense %s (torch.matmul) done: %.3f ms" % (r["product"], r["ms"]), file=sys.stderr,
+        print("# dense %s (hipBLASLt) done: %.3f ms" % (r["product"], r["ms"]), file=sys.stderr,
               flush=True)
     for r in stack or []:
         print("# %s done: %.1f ms/step" % (r["workload"], r["ms_per_step"]), file=sys.stderr,
