@@ -168,13 +168,13 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const T* __restrict__ 
 // read all of W_g once per token), and its 4 wavefronts split the features:
 // lane l of wave w accumulates the 8-wide chunks 64 w + l, 64 w + l + 256,
 // ... of each token.  (One wavefront per 4 tokens left one wave per SIMD
-// at T = 4096 and ran 3x longer: every load round trip was exposed.)  After
+// at T = 4096 and ran 1.4x longer: its load round trips were exposed.)  After
 // the transposed butterfly lane l holds expert l / 8 of the wave's partial;
 // the 4 partials are added in wave order through LDS.  Top-K then runs for
 // the 4 tokens at once in wave 0: lane 16 n + e (e < 8) holds expert e of
 // token n, and K rounds of an arg-max over each 16-lane group pick the
 // experts with key (-logit, index), as in the general kernel.
-constexpr int kRouterTokPerWave = 4;
+constexpr int kRouterTokPerGroup = 4;
 
 __global__ __launch_bounds__(256) void router_e8_kernel(const bf16_t* __restrict__ x,
                                                         const bf16_t* __restrict__ Wg, int T_,
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256) void router_e8_kernel(const bf16_t* __restrict
                                                         int32_t* __restrict__ topk_idx,
                                                         float* __restrict__ topk_w,
                                                         float* __restrict__ logits_out) {
-  constexpr int NT = kRouterTokPerWave;
+  constexpr int NT = kRouterTokPerGroup;
   __shared__ float part[4][NT][8];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -288,7 +288,7 @@ hipError_t launch_router_topk(const void* x, const void* Wg, int T, int d, int E
                    (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(Wg) & 15) == 0;
   if (dtype == kBF16 && vec && !wide && E == 8 && K <= 8) {
-    const int per_block = kRouterTokPerWave;
+    const int per_block = kRouterTokPerGroup;
     hipLaunchKernelGGL(router_e8_kernel, dim3((T + per_block - 1) / per_block), dim3(256), 0,
                        stream, static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(Wg), T, d,
                        K, topk_idx, topk_w, logits);
