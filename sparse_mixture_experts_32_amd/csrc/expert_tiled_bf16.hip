@@ -24,18 +24,19 @@
 //     the loads in flight to the other slots; waits are explicit vmcnt counts
 //     followed by a bare s_barrier;
 //   * 256 weight columns x 256 tokens per workgroup (with W1/W3: 128 H
-//     features of each), eight waves of 128 x 64 (two per SIMD, so one
-//     wave's matrix instructions cover the other's LDS reads),
+//     features of each), eight waves of 128 x 64 (two per SIMD),
 //     v_mfma_f32_16x16x32_bf16 with fp32 accumulators; D is
 //     [feature][token], so the epilogue writes 4 consecutive features per
 //     lane (SiLU(a) * b fused for W1/W3);
-//   * per k-stage a wave reads its fragments, then its 32 matrix instructions
-//     run with the stage's four load issues spread between them (one ahead
-//     of every 8), so the vector-memory queue drains while the matrix cores
-//     work instead of stalling the wave right after the barrier; the k loop
-//     is instantiated twice -- one straight block for tiles whose token
-//     groups are all live, one that skips the groups lying wholly in the
-//     padding of an expert's last tile;
+//   * ping-pong: per k-stage a wave has a read phase (its LDS fragment
+//     reads, then the stage's four load issues) and a matrix phase (its 32
+//     matrix instructions), separated by barriers, and waves 4-7 run one
+//     barrier behind waves 0-3, so on each SIMD one wave multiplies while
+//     the other reads (3-4 % faster than all eight waves reading and then
+//     multiplying together); the k loop is instantiated for both groups and
+//     twice per group -- one straight block for tiles whose token groups are
+//     all live, one that skips the groups lying wholly in the padding of an
+//     expert's last tile;
 //   * tile order: each XCD runs a contiguous range in which 4 feature tiles
 //     are interleaved with the token tiles, so the ~32 workgroups it runs at
 //     once share a few weight tiles and a few token tiles in its L2.
@@ -92,6 +93,11 @@ template <int n>
 __device__ __forceinline__ void wait_vm() {
   static_assert(n >= 0 && n < 64, "vmcnt");
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt lgkmcnt(0) only.
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
 }
 
 template <int BT, bool DUAL>
@@ -262,13 +268,7 @@ __global__ __launch_bounds__(128 * kWavesT) void tiled_gemm_kernel(TiledArgs arg
 #pragma unroll
         for (int jb = 0; jb < C::kNJ; ++jb)
           acc[i][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[jb], acc[i][jb], 0, 0, 0);
-      // ds reads first, then each load issue ahead of 8 matrix instructions
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::kMI + C::kNJ, 0);
-#pragma unroll
-      for (int q = 0; q < C::kDmaPerStage; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one load issue
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // 8 matrix instructions
-      }
+
     } else {
 #pragma unroll
       for (int jb = 0; jb < C::kNJ; ++jb) {
@@ -288,26 +288,60 @@ __global__ __launch_bounds__(128 * kWavesT) void tiled_gemm_kernel(TiledArgs arg
 #pragma unroll
   for (int s = 0; s < kSlots - 1; ++s) issue(s, sW[s], sA[s]);
 
-  auto k_loop = [&](auto full_tag) {
+  // Ping-pong: waves 0-3 (group A) and 4-7 (group B); with waves dealt to
+  // the four SIMDs round-robin, each SIMD holds one wave of each group.  Each stage has a read phase (LDS reads, load
+  // issues) and a matrix phase, separated by barriers; group B runs one
+  // barrier behind group A, so on every SIMD one wave multiplies while the
+  // other reads.  A workgroup barrier counts arrivals, so A's read barrier of
+  // stage k pairs with B's matrix barrier of stage k-1, and B's read barrier
+  // of stage k with A's matrix barrier of stage k.  Hence B's loads of stage
+  // k+1 must have landed when B reaches its matrix barrier of stage k (A reads
+  // stage k+1 right after it), and every wave's reads of a slot have returned
+  // before the barrier that lets another wave refill it.
+  const bool group_b = wave >= 4;
+  constexpr int kLead = (kSlots - 2) * C::kDmaPerStage;
+  if (group_b) {
+    wait_vm<kLead>();                 // own stage 0 landed
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  auto k_loop = [&](auto full_tag, auto b_tag) {
+    constexpr bool GB = decltype(b_tag)::value;
     for (int k0 = 0; k0 < nk; k0 += kSlots) {
 #pragma unroll
       for (int s = 0; s < kSlots; ++s) {
         const int kt = k0 + s;
-        wait_vm<(kSlots - 2) * C::kDmaPerStage>();   // stage kt landed; later ones may not have
-        __builtin_amdgcn_s_barrier();                // ... for every wave; slot of kt-1 is free
-        // read this slot's operands, refill the slot every wave finished
-        // reading in the previous stage, multiply
+        // A: own stage kt landed.  B: already true (waited before its last
+        // matrix barrier); the no-op wait tells the compiler so.
+        wait_vm<kLead>();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
         read_frags(sW[s], sA[s]);
+        __builtin_amdgcn_sched_barrier(0);
         issue(min(kt + kSlots - 1, nk - 1), sW[(s + kSlots - 1) % kSlots],
               sA[(s + kSlots - 1) % kSlots]);
+        wait_lgkm0();                          // this wave's reads returned
+        if constexpr (GB) wait_vm<kLead>();    // own stage kt+1 landed
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
         mma(full_tag);
       }
     }
   };
-  if (live_groups == C::kNJ)
-    k_loop(std::true_type{});
-  else
-    k_loop(std::false_type{});
+  if (live_groups == C::kNJ) {
+    if (group_b) k_loop(std::true_type{}, std::true_type{});
+    else k_loop(std::true_type{}, std::false_type{});
+  } else {
+    if (group_b) k_loop(std::false_type{}, std::true_type{});
+    else k_loop(std::false_type{}, std::false_type{});
+  }
+  if (!group_b) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();       // pairs with B's last matrix barrier
+  }
   wait_vm<0>();  // no load may land in LDS after the workgroup ends
 
   // ---- epilogue: lane holds features f .. f+3 of token column j ----
