@@ -391,8 +391,10 @@ hipError_t launch_tiled(const TiledArgs& in, int P, hipStream_t stream) {
 
 }  // namespace
 
-bool tiled_gemm_supported(int Kdim, int N, bool dual, int splits) {
-  return splits >= 1 && Kdim % (kBK * kSlots * splits) == 0 && N % (dual ? kBF / 2 : kBF) == 0;
+bool tiled_gemm_supported(int Kdim, int N, bool dual, int splits, int64_t a_rows) {
+  // token-operand byte offsets are 32-bit per lane
+  return splits >= 1 && Kdim % (kBK * kSlots * splits) == 0 && N % (dual ? kBF / 2 : kBF) == 0 &&
+         a_rows * Kdim * 2 < (int64_t(1) << 32);
 }
 
 int tiled_gemm_tiles(int P, int E, int N, bool dual) {

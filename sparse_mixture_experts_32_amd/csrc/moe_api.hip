@@ -83,10 +83,10 @@ Plan make_plan(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K, int32_t
   const int64_t P = T * K;
   if (dt != MOE_BF16 || P == 0) return p;
   if (P > 64) {
-    if (moe::tiled_gemm_supported((int)d_ff, (int)d, false, 1)) {
+    if (moe::tiled_gemm_supported((int)d_ff, (int)d, false, 1, P)) {
       const int64_t tiles = moe::tiled_gemm_tiles((int)P, E, (int)d, false);
       for (int s = 2; s <= 4 && tiles * (s - 1) < 4 * 256; ++s)
-        if (moe::tiled_gemm_supported((int)d_ff, (int)d, false, s)) p.down_splits = s;
+        if (moe::tiled_gemm_supported((int)d_ff, (int)d, false, s, P)) p.down_splits = s;
     }
     return p;
   }
@@ -255,7 +255,7 @@ hipError_t run_swiglu(const Plan& plan, const void* x, const int32_t* sorted_tok
   if (plan.streaming)
     return moe::launch_stream_swiglu_bf16(x, sorted_token, p1, p3, offsets, P, d, d_ff, E,
                                           plan.swiglu_splits, static_cast<float*>(scratch), H, st);
-  if (moe::tiled_gemm_supported(d, d_ff, true, 1))
+  if (moe::tiled_gemm_supported(d, d_ff, true, 1, P))
     return moe::launch_tiled_swiglu_bf16(x, sorted_token, p1, p3, offsets, P, d, d_ff, E, H, st);
   return moe::launch_expert_swiglu_bf16(x, sorted_token, p1, p3, offsets, P, d, d_ff, E, H, st);
 }
@@ -266,7 +266,7 @@ hipError_t run_down(const Plan& plan, const void* H, const moe::ExpertPtrs& p2,
   if (dtype != MOE_BF16) return moe::launch_expert_down_f32(H, p2, offsets, P, d, d_ff, E, O, st);
   if (plan.streaming)
     return moe::launch_stream_down_bf16(H, p2, offsets, P, d, d_ff, E, plan.down_splits, O, st);
-  if (moe::tiled_gemm_supported(d_ff, d, false, plan.down_splits))
+  if (moe::tiled_gemm_supported(d_ff, d, false, plan.down_splits, P))
     return moe::launch_tiled_down_bf16(H, p2, offsets, P, d, d_ff, E, plan.down_splits, O, st);
   return moe::launch_expert_down_bf16(H, p2, offsets, P, d, d_ff, E, O, st);
 }

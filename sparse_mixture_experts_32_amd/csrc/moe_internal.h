@@ -60,7 +60,9 @@ hipError_t launch_stream_down_bf16(const void* H, const ExpertPtrs& W2, const in
 
 // CDNA4 tiled variants for large batches (direct-to-LDS loads, transposed
 // LDS reads); need Kdim % 128 == 0 and N % 128 (W1/W3) or N % 256 (W2).
-bool tiled_gemm_supported(int Kdim, int N, bool dual, int splits);
+// a_rows: rows of the token operand (x or H); their byte offsets must fit
+// 32 bits, else the grouped kernels of expert_gemm_bf16.hip take the product.
+bool tiled_gemm_supported(int Kdim, int N, bool dual, int splits, int64_t a_rows);
 int tiled_gemm_tiles(int P, int E, int N, bool dual);  // worst-case workgroups per split
 hipError_t launch_tiled_swiglu_bf16(const void* x, const int32_t* sorted_token,
                                     const ExpertPtrs& W1, const ExpertPtrs& W3,

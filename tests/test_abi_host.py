@@ -62,6 +62,11 @@ def test_plan(lib):
     p = M.plan_for(4096, 4096, 14336, 8, 2, M.BF16)
     assert not p["streaming"] and p["swiglu_splits"] == 0 and p["swiglu_scratch_bytes"] == 0
     assert p["down_splits"] >= 1 and 14336 % (128 * p["down_splits"]) == 0
+    # the tiled W2 kernel addresses its token operand (H) with 32-bit byte
+    # offsets: at d_ff = 65536, 32000 rows fit (K split 4), 33000 do not and
+    # W2 falls back to the unsplit grouped kernel
+    assert M.plan_for(16000, 256, 65536, 8, 2, M.BF16)["down_splits"] == 4
+    assert M.plan_for(16500, 256, 65536, 8, 2, M.BF16)["down_splits"] == 1
     p = M.plan_for(8, 128, 256, 8, 2, M.F32)
     assert not p["streaming"]
 

@@ -369,6 +369,23 @@ def test_full_decode_small_batches(dev, T):
     _full(w, dev, tokens=range(T))
 
 
+def test_tiled_operand_past_32_bit_offsets_takes_grouped_kernels(dev):
+    """d_ff = 65536 at T = 16500 (K = 2) makes H 33000 rows x 128 KB: its byte
+    offsets pass 2^32, beyond the tiled kernel's 32-bit lane offsets, so the
+    W2 product goes to the grouped kernels.  Tokens whose sorted rows lie past
+    that point are checked against the oracle."""
+    w = small(T=16500, d=256, d_ff=65536)
+    say("32-bit offset limit", w.T, w.d, w.d_ff, M.plan_for(w.T, w.d, w.d_ff, w.E, w.K, M.BF16))
+    inp = W.layer_inputs(w, dev)
+    _, v = run_forward(inp, w.K)
+    pos = v["pos"].cpu().numpy()
+    del v
+    late = np.nonzero(pos.max(axis=1).astype(np.int64) * w.d_ff * 2 >= 2 ** 32)[0]
+    assert late.size > 0
+    tokens = np.concatenate([late[:: max(1, late.size // 8)][:8], [0, w.T - 1]])
+    check_layer(inp, w.K, tokens=np.unique(tokens), bf16_store=False)
+
+
 def test_full_T512_sampled(dev):
     _full("mid_bf16_T512", dev, tokens=np.random.default_rng(1).choice(512, 32, replace=False))
 
