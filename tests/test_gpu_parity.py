@@ -437,13 +437,15 @@ def test_stack_small_vs_oracle(dev, dtype):
     assert max_rel <= layers * tol and l2_rel <= tol
 
 
-def test_stack_graph_replay_matches_eager(dev):
-    """The whole decode-size stack step captured in one HIP graph: every
-    replay, with eager work and synchronisations between replays, gives the
-    eager result bit for bit (the library allocates and memsets nothing, so
-    the captured step is only its kernels)."""
-    w = small(name="stack32_bf16_T4096", T=8, d=256, d_ff=512, dtype="bf16")
-    say("stack graph replay")
+@pytest.mark.parametrize("T", [8, 300])
+def test_stack_graph_replay_matches_eager(dev, T):
+    """A whole stack step captured in one HIP graph: every replay, with eager
+    work and synchronisations between replays, gives the eager result bit for
+    bit (the library allocates and memsets nothing, so the captured step is
+    only its kernels).  T = 8 takes the streaming kernels, T = 300 the tiled
+    ping-pong ones."""
+    w = small(name="stack32_bf16_T4096", T=T, d=256, d_ff=512, dtype="bf16")
+    say("stack graph replay", T, M.plan_for(T, 256, 512, w.E, w.K, M.BF16))
     h0, blocks = _stack_inputs(w, dev, 3)
     ws = torch.empty(M.workspace_size(w.T, w.d, w.d_ff, w.E, w.K, M.BF16), dtype=torch.uint8,
                      device=dev)
