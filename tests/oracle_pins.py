@@ -370,6 +370,97 @@ def check_faithful_close_to_exact():
     assert 0 < rel < 2e-2
 
 
+def _one_expert(W1, W3, W2):
+    """One expert, so with K = 1 the gate weight is exactly 1 whatever the
+    router says (softmax over a single selected logit)."""
+    d = np.asarray(W1).shape[0]
+    return np.zeros((d, 1)), [np.asarray(W1, float)], [np.asarray(W3, float)], \
+        [np.asarray(W2, float)]
+
+
+def check_faithful_rounds_h_hand():
+    """Faithful mode rounds the SwiGLU product H to bfloat16 before the W2
+    projection (code block D run in bfloat16 stores H in the activation
+    dtype), and nothing else inside the expert.  Hand case, d = 1, d_ff = 2:
+      x = [1]; W1 = [[64, 64]] so a = 64 and SiLU(64) = 64 / (1 + e^-64) = 64
+      exactly in binary64 (e^-64 < 2^-53); W3 = [[(1 + 3 2^-9) / 64,
+      (1 + 2^-9) / 64]] so H = [1 + 3 2^-9, 1 + 2^-9] exactly; W2 = [[1], [-1]].
+      bf16 spacing above 1 is 2^-7: bf16(1 + 3 2^-9) = 1 + 2^-7 (three
+      quarters of a spacing rounds up), bf16(1 + 2^-9) = 1 (a quarter rounds
+      down).  Faithful y = 2^-7; exact y = 2 2^-9 = 2^-8.  Rounding the
+      expert output instead of H would give bf16(2^-8) = 2^-8."""
+    W_g, W1s, W3s, W2s = _one_expert([[64.0, 64.0]],
+                                     [[(1 + 3 * 2.0 ** -9) / 64, (1 + 2.0 ** -9) / 64]],
+                                     [[1.0], [-1.0]])
+    x = np.array([[1.0]])
+    yf, aux = O.moe_forward(x, W_g, W1s, W3s, W2s, K=1, faithful=True)
+    ye, _ = O.moe_forward(x, W_g, W1s, W3s, W2s, K=1, faithful=False)
+    assert aux["w"][0, 0] == 1.0
+    assert yf[0, 0] == 2.0 ** -7, yf
+    assert ye[0, 0] == 2.0 ** -8, ye
+    # same case with W2 = I (d_ff = d = 2): faithful y is bf16(H) itself
+    W_g2, W1s2, W3s2, W2s2 = _one_expert([[64.0, 64.0], [0.0, 0.0]],
+                                         [[(1 + 3 * 2.0 ** -9) / 64, (1 + 2.0 ** -9) / 64],
+                                          [0.0, 0.0]], np.eye(2))
+    yf2, _ = O.moe_forward(np.array([[1.0, 0.0]]), W_g2, W1s2, W3s2, W2s2, K=1, faithful=True)
+    assert yf2.tolist() == [[1.0 + 2.0 ** -7, 1.0]], yf2
+
+
+def check_stack_prenorm_hand():
+    """One pre-norm block in the order of the slide "Architecture – 全体"
+    (RMSNorm, then the mixture of experts, then the residual add), by hand
+    with eps = 0, one expert and K = 1:
+      h0 = [2, -2]: mean(h0^2) = 4, RMSNorm(h0) = [1, -1]
+      W1 = [[64], [0]]: a = 64, SiLU(64) = 64 exactly; W3 = [[0.5], [0]]: b = 0.5
+      H = 32; W2 = [[1/64, 1/32]]: MoE = [0.5, 1]; h1 = h0 + MoE = [2.5, -1].
+    A block that fed h0 itself to the MoE would get a = 128 and h1 = [4, 2].
+    Faithful mode rounds the new residual stream to bfloat16: with
+    W2 = [[3 2^-13, 1/32]] the MoE adds [3 2^-8, 1]; 2 + 3 2^-8 is three
+    quarters of a bf16 spacing (2^-6) above 2, so h1 = [2 + 2^-6, -1]
+    (exact mode: [2 + 3 2^-8, -1])."""
+    h0 = np.array([[2.0, -2.0]])
+    blk = _one_expert([[64.0], [0.0]], [[0.5], [0.0]], [[1 / 64, 1 / 32]])
+    h1, _ = O.stack_forward(h0, [blk], K=1, eps=0.0)
+    assert h1.tolist() == [[2.5, -1.0]], h1
+    blk = _one_expert([[64.0], [0.0]], [[0.5], [0.0]], [[3 * 2.0 ** -13, 1 / 32]])
+    h1e, _ = O.stack_forward(h0, [blk], K=1, eps=0.0)
+    h1f, _ = O.stack_forward(h0, [blk], K=1, eps=0.0, faithful=True)
+    assert h1e.tolist() == [[2.0 + 3 * 2.0 ** -8, -1.0]], h1e
+    assert h1f.tolist() == [[2.0 + 2.0 ** -6, -1.0]], h1f
+
+
+def check_stack_two_blocks_hand():
+    """Two blocks applied in order, each reading the residual stream the
+    previous one left (eps = 0, one expert, K = 1):
+      block 1 on h0 = [2, -2]: RMSNorm = [1, -1], W1 = [[64], [0]] (a = 64),
+        W3 = [[0.5], [0]] (H = 32), W2 = [[0, 1/8]]: adds [0, 4] -> h1 = [2, 2]
+      block 2 on h1: RMSNorm = [1, 1], W1 = [[32], [32]] (a = 64),
+        W3 = [[0.5], [0.5]] (H = 64), W2 = [[1/64, 1/64]]: adds [1, 1] -> [3, 3].
+    Both blocks reading h0, or the blocks in reverse order, give [2, 2]
+    (block 2 sees RMSNorm(h0) = [1, -1], a = 0, SiLU(0) = 0)."""
+    h0 = np.array([[2.0, -2.0]])
+    b1 = _one_expert([[64.0], [0.0]], [[0.5], [0.0]], [[0.0, 1 / 8]])
+    b2 = _one_expert([[32.0], [32.0]], [[0.5], [0.5]], [[1 / 64, 1 / 64]])
+    h2, margins = O.stack_forward(h0, [b1, b2], K=1, eps=0.0)
+    assert h2.tolist() == [[3.0, 3.0]], h2
+    assert len(margins) == 2
+
+
+def check_stack_scale_invariance():
+    """With eps = 0, RMSNorm(c h) = RMSNorm(h) for c > 0, exactly in binary64
+    when c is a power of two; so one pre-norm block adds the same MoE output
+    to c h0 as to h0 (the block's input is normalised before the MoE, slide
+    "Architecture – 全体").  A block whose MoE read anything that is not
+    scale invariant fails this."""
+    x, W_g, W1s, W3s, W2s = tiny_layer(17, T=6, d=6, d_ff=5, E=4)
+    h1, _ = O.stack_forward(x, [(W_g, W1s, W3s, W2s)], K=2, eps=0.0)
+    y = h1 - x
+    assert np.abs(y).max() > 1e-3
+    for c in (2.0 ** 5, 2.0 ** -3):
+        hc, _ = O.stack_forward(c * x, [(W_g, W1s, W3s, W2s)], K=2, eps=0.0)
+        assert np.allclose(hc - c * x, y, rtol=0, atol=1e-13 * max(c, 1.0))
+
+
 def check_rmsnorm_closed_form():
     for c in (0.5, -3.0, 1e-3):
         h = np.full((1, 16), c)

@@ -61,6 +61,60 @@ def _router_transposed(x, W_g):
     return x @ W[::-1]
 
 
+def _swiglu_rounds_output(x_rows, W1, W3, W2, faithful=False):
+    x_rows = np.asarray(x_rows, dtype=np.float64)
+    a = x_rows @ np.asarray(W1, dtype=np.float64)
+    h = O.silu(a) * (x_rows @ np.asarray(W3, dtype=np.float64))
+    out = h @ np.asarray(W2, dtype=np.float64)
+    return O.bf16_round(out) if faithful else out
+
+
+def _stack_moe_reads_h(h0, blocks, K, eps=1e-5, faithful=False):
+    h = np.asarray(h0, dtype=np.float64)
+    margins = []
+    for (W_g, W1s, W3s, W2s) in blocks:
+        y, aux = O.moe_forward(h, W_g, W1s, W3s, W2s, K, faithful)
+        margins.append(O.routing_margins(aux["logits"], K))
+        h = h + y
+        if faithful:
+            h = O.bf16_round(h)
+    return h, margins
+
+
+def _stack_post_norm(h0, blocks, K, eps=1e-5, faithful=False):
+    h = np.asarray(h0, dtype=np.float64)
+    margins = []
+    for (W_g, W1s, W3s, W2s) in blocks:
+        y, aux = O.moe_forward(h, W_g, W1s, W3s, W2s, K, faithful)
+        margins.append(O.routing_margins(aux["logits"], K))
+        h = O.rmsnorm(h + y, eps, faithful)
+    return h, margins
+
+
+def _stack_blocks_read_h0(h0, blocks, K, eps=1e-5, faithful=False):
+    h0 = np.asarray(h0, dtype=np.float64)
+    xn = O.rmsnorm(h0, eps, faithful)
+    h = h0.copy()
+    margins = []
+    for (W_g, W1s, W3s, W2s) in blocks:
+        y, aux = O.moe_forward(xn, W_g, W1s, W3s, W2s, K, faithful)
+        margins.append(O.routing_margins(aux["logits"], K))
+        h = h + y
+        if faithful:
+            h = O.bf16_round(h)
+    return h, margins
+
+
+def _stack_no_residual_rounding(h0, blocks, K, eps=1e-5, faithful=False):
+    h = np.asarray(h0, dtype=np.float64)
+    margins = []
+    for (W_g, W1s, W3s, W2s) in blocks:
+        y, aux = O.moe_forward(O.rmsnorm(h, eps, faithful), W_g, W1s, W3s, W2s, K, faithful)
+        margins.append(O.routing_margins(aux["logits"], K))
+        h = h + y
+    return h, margins
+
+
 _orig_swiglu = O.swiglu_expert
 _orig_route = O.route_tables
 _orig_gate_weights = O.gate_weights
@@ -75,6 +129,11 @@ MUTATIONS = {
     "gate_ranks_swapped": ("gate_weights", _gate_weights_rank_swap),
     "bf16_truncates": ("bf16_round", _bf16_truncate),
     "router_operand_flipped": ("router_logits", _router_transposed),
+    "faithful_rounds_expert_output": ("swiglu_expert", _swiglu_rounds_output),
+    "stack_moe_reads_unnormalised_h": ("stack_forward", _stack_moe_reads_h),
+    "stack_post_norm": ("stack_forward", _stack_post_norm),
+    "stack_every_block_reads_h0": ("stack_forward", _stack_blocks_read_h0),
+    "stack_faithful_skips_residual_rounding": ("stack_forward", _stack_no_residual_rounding),
 }
 
 
