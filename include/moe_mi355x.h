@@ -150,7 +150,11 @@ moe_status moe_router_topk(const void* x, const void* W_g, int64_t T, int64_t d,
  * processes): stable counting sort of the T*K pairs p = t*K + r by expert.
  *   offsets int32 [E+1]; sorted_token int32 [T*K] (token ascending inside a
  *   segment); pos int32 [T, K] = sorted position of pair (t, r).
- * Bit-exact and deterministic.
+ * Bit-exact and deterministic.  A pair whose expert index lies outside
+ * [0, E) is dropped: it belongs to no segment (offsets[E] counts only the
+ * kept pairs) and gets pos = -1, which moe_combine reads as "adds nothing".
+ * moe_router_topk writes such an index (-1) only for a token whose logits
+ * are not finite, which the finite-input contract excludes.
  */
 moe_status moe_route_permute(const int32_t* topk_idx, int64_t T, int32_t E, int32_t K,
                              int32_t* offsets, int32_t* sorted_token, int32_t* pos,
@@ -195,6 +199,8 @@ moe_status moe_expert_down(const void* H, const void* const* W2, int64_t T, int6
  * o_r = sum over s < o_splits of O[s][pos[t,r]] (in s order), then
  * s = w[t,0]*o_0 and s = fma(w[t,r], o_r, s) for r = 1..K-1, in fp32;
  * y[t] = round(s), or round(y[t] + s) when accumulate = 1.
+ * pos[t,r] must be -1 or a row of O (< the rows of one slice); a pair with
+ * pos = -1 (dropped by moe_route_permute) contributes o_r = 0.
  */
 moe_status moe_combine(const float* O, int32_t o_splits, const float* topk_w, const int32_t* pos,
                        int64_t T, int64_t d, int32_t K, void* y, int32_t y_dtype,

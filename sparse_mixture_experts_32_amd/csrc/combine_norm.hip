@@ -7,8 +7,8 @@
 // gathers its K expert rows O[pos[t, r]] (each the sum of the K-split slices
 // of the W2 product, added in slice order) and sums them in rank order in fp32
 // with one fixed expression, s = w0*O0, then s = fma(w_r, O_r, s); y is rounded
-// once (after adding the residual in accumulate mode).  No atomics: bitwise
-// reproducible.
+// once (after adding the residual in accumulate mode).  A pair with pos < 0
+// (dropped by the dispatch) adds nothing.  No atomics: bitwise reproducible.
 //
 // RMSNorm: "【DL輪読会】Mixtral of Experts" (docswell slides), slide
 // "Architecture – 全体" (RMSNorm ahead of the mixture of experts); unit gain.
@@ -30,8 +30,13 @@ __device__ __forceinline__ float load_y<bf16_t>(const bf16_t* y, int64_t i) {
 __device__ __forceinline__ void store_y(float* y, int64_t i, float v) { y[i] = v; }
 __device__ __forceinline__ void store_y(bf16_t* y, int64_t i, float v) { y[i] = f32_to_bf16(v); }
 
-// Sum of the o_splits slices of O at element i, in slice order.
-__device__ __forceinline__ float4 load_o4(const float* O, int splits, int64_t slice, int64_t i) {
+// Sum of the o_splits slices of O at features c..c+3 of sorted row p, in
+// slice order.  A pair the dispatch dropped (pos = -1: its expert index was
+// outside [0, E)) has no row and contributes zeros.
+__device__ __forceinline__ float4 load_o4(const float* O, int splits, int64_t slice, int32_t p,
+                                          int d, int c) {
+  if (p < 0) return make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  const int64_t i = (int64_t)p * d + c;
   float4 v = *reinterpret_cast<const float4*>(O + i);
   for (int s = 1; s < splits; ++s) {
     const float4 u = *reinterpret_cast<const float4*>(O + s * slice + i);
@@ -43,7 +48,10 @@ __device__ __forceinline__ float4 load_o4(const float* O, int splits, int64_t sl
   return v;
 }
 
-__device__ __forceinline__ float load_o1(const float* O, int splits, int64_t slice, int64_t i) {
+__device__ __forceinline__ float load_o1(const float* O, int splits, int64_t slice, int32_t p,
+                                        int d, int c) {
+  if (p < 0) return 0.0f;
+  const int64_t i = (int64_t)p * d + c;
   float v = O[i];
   for (int s = 1; s < splits; ++s) v += O[s * slice + i];
   return v;
@@ -63,11 +71,11 @@ __global__ __launch_bounds__(256) void combine_vec4_kernel(const float* __restri
     const int c = (int)(g % (d / 4)) * 4;
     const float* wt = topk_w + (int64_t)t * K;
     const int32_t* pt = pos + (int64_t)t * K;
-    const float4 o0 = load_o4(O, splits, slice, (int64_t)pt[0] * d + c);
+    const float4 o0 = load_o4(O, splits, slice, pt[0], d, c);
     const float w0 = wt[0];
     float s0 = w0 * o0.x, s1 = w0 * o0.y, s2 = w0 * o0.z, s3 = w0 * o0.w;
     for (int r = 1; r < K; ++r) {
-      const float4 o = load_o4(O, splits, slice, (int64_t)pt[r] * d + c);
+      const float4 o = load_o4(O, splits, slice, pt[r], d, c);
       const float w = wt[r];
       s0 = fmaf(w, o.x, s0);
       s1 = fmaf(w, o.y, s1);
@@ -107,8 +115,8 @@ __global__ __launch_bounds__(256) void combine_scalar_kernel(const float* __rest
     const int c = (int)(g % d);
     const float* wt = topk_w + (int64_t)t * K;
     const int32_t* pt = pos + (int64_t)t * K;
-    float s = wt[0] * load_o1(O, splits, slice, (int64_t)pt[0] * d + c);
-    for (int r = 1; r < K; ++r) s = fmaf(wt[r], load_o1(O, splits, slice, (int64_t)pt[r] * d + c), s);
+    float s = wt[0] * load_o1(O, splits, slice, pt[0], d, c);
+    for (int r = 1; r < K; ++r) s = fmaf(wt[r], load_o1(O, splits, slice, pt[r], d, c), s);
     if (ACC) s = load_y(y, g) + s;
     store_y(y, g, s);
   }

@@ -196,6 +196,52 @@ def test_permute_all_to_one_expert(dev):
     assert st.cpu().tolist() == r_st.tolist() and pos.cpu().numpy().tolist() == r_pos.tolist()
 
 
+@pytest.mark.parametrize("T,E,K,splits", [(37, 4, 2, 1), (1500, 8, 2, 2)])
+def test_dropped_pairs_add_nothing(dev, T, E, K, splits):
+    """Expert indices outside [0, E) (written by the router only for
+    non-finite logits) are dropped: the dispatch leaves them out of every
+    segment and gives them pos = -1, and the combine adds nothing for them.
+    T = 37 takes the streaming dispatch, T = 1500 (3000 pairs) the held one."""
+    say("dropped pairs", T, E, K, splits)
+    idx = random_routing(T, E, K, seed=T + 17)
+    planted = [(3, K - 1, E), (10, 0, -1), (20, 0, E + 2), (20, K - 1, -7), (T - 1, 0, 1 << 20)]
+    for t, r, v in planted:
+        idx[t, r] = v
+    off, st, pos = M.moe_route_permute(idx.to(torch.int32).to(dev), E)
+    torch.cuda.synchronize()
+    idx_np = idx.numpy()
+    kept = [(p // K, p % K) for p in range(T * K) if 0 <= idx_np[p // K, p % K] < E]
+    order = sorted(range(len(kept)), key=lambda i: idx_np[kept[i]])     # stable
+    ref_off = np.zeros(E + 1, dtype=np.int64)
+    for t, r in kept:
+        ref_off[idx_np[t, r] + 1] += 1
+    ref_off = np.cumsum(ref_off)
+    ref_pos = np.full((T, K), -1, dtype=np.int64)
+    for dest, i in enumerate(order):
+        ref_pos[kept[i]] = dest
+    assert off.cpu().numpy().tolist() == ref_off.tolist()
+    assert st.cpu().numpy()[:len(kept)].tolist() == [kept[i][0] for i in order]
+    assert pos.cpu().numpy().tolist() == ref_pos.tolist()
+    # combine: a dropped pair contributes exactly what a kept pair of weight
+    # zero would (s = w0*o0, then s = fma(w, o, s), and fma(0, o, s) = s)
+    g = torch.Generator(device="cpu").manual_seed(T)
+    O_ = torch.randn((splits, T * K, 256), generator=g).to(dev)
+    wts = torch.rand((T, K), generator=g).to(dev)
+    y_drop = M.moe_combine(O_, wts, pos)
+    dropped = pos < 0
+    y_zero = M.moe_combine(O_, torch.where(dropped, torch.zeros_like(wts), wts),
+                           torch.where(dropped, torch.zeros_like(pos), pos))
+    h = torch.randn((T, 256), generator=g).to(dev).to(torch.bfloat16)
+    h_drop = M.moe_combine(O_, wts, pos, y=h.clone(), accumulate=True)
+    h_zero = M.moe_combine(O_, torch.where(dropped, torch.zeros_like(wts), wts),
+                           torch.where(dropped, torch.zeros_like(pos), pos), y=h.clone(),
+                           accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y_drop).all()
+    assert torch.equal(y_drop, y_zero) and torch.equal(h_drop, h_zero)
+    assert torch.all(y_drop[20] == 0)                  # both of token 20's pairs dropped
+
+
 # ---------------------------------------------------------------- layer
 def test_layer_tiny_f32(dev):
     w = W.WORKLOADS["tiny_f32_T64"]

@@ -11,8 +11,10 @@ follows the routing analysis reported in "杀疯了的开源专家模型 Mixtral
 论文公开啦！" (redian.news), section "实验" (consecutive tokens often share an
 expert).  Every tensor has its own seed, derived from the workload seed and the
 tensor's name, so any one matrix can be regenerated alone.  Values are drawn in
-float32 with torch's seeded generators (on the device given) and rounded to
-bfloat16 by torch's round-to-nearest-even conversion.
+float32 with torch's seeded generators and rounded to bfloat16 by torch's
+round-to-nearest-even conversion.  The routing inputs (token rows and router
+weights) are drawn on the host and copied, so a workload routes the same way
+on every device; the expert matrices are drawn on the device that holds them.
 """
 
 from __future__ import annotations
@@ -24,11 +26,12 @@ import numpy as np
 import torch
 
 # Per-expert router bias of the skewed prefill workload: makes the share of
-# (token, expert) pairs of expert e follow Zipf(1.2) over 8 experts.  Written
-# by ``python -m oracle.calibrate_zipf_bias`` (fixed-point iteration on
-# standard-normal logits).
-ZIPF_BIAS = (1.766886, 0.446202, 0.064144, -0.178101,
-             -0.346527, -0.482479, -0.58561, -0.684514)
+# (token, expert) pairs of expert e follow Zipf(1.2) over 8 experts, within
+# 0.5 % on the 4096-token instance.  Written by
+# ``python -m oracle.calibrate_zipf_bias`` (fixed-point iteration, first on
+# standard-normal logits, then on the instance's own rows).
+ZIPF_BIAS = (1.750051, 0.431113, 0.098852, -0.128279,
+             -0.280979, -0.506476, -0.630174, -0.734108)
 
 
 @dataclass(frozen=True)
@@ -99,10 +102,12 @@ def _unit_rms_rows(t: torch.Tensor) -> torch.Tensor:
 
 def expert_weights(w: Workload, device="cpu", block: int = 0, experts=None):
     """(W_g, W1s, W3s, W2s) of one block.  W_g [d, E], W1/W3 [d, d_ff],
-    W2 [d_ff, d]; every entry N(0, 1/fan_in)."""
+    W2 [d_ff, d]; every entry N(0, 1/fan_in).  W_g is drawn on the host and
+    copied to ``device`` (the routing inputs are the same bytes whatever the
+    device); the expert matrices are drawn on ``device``."""
     dt = w.torch_dtype
     experts = range(w.E) if experts is None else experts
-    W_g = _normal((w.d, w.E), w.d ** -0.5, device, _seed(w.seed, block, "W_g"), dt)
+    W_g = _normal((w.d, w.E), w.d ** -0.5, "cpu", _seed(w.seed, block, "W_g"), dt).to(device)
     W1s, W3s, W2s = [], [], []
     for e in experts:
         W1s.append(_normal((w.d, w.d_ff), w.d ** -0.5, device, _seed(w.seed, block, "W1", e), dt))
@@ -131,27 +136,43 @@ def fold_bias(W_g: torch.Tensor, b) -> torch.Tensor:
     return torch.from_numpy(u)
 
 
+def zipf_rows(w: Workload, block: int = 0, T: int | None = None) -> torch.Tensor:
+    """The skewed recipe's rows before the router bias, float32 on the host:
+    runs of Geom(0.3) length share a base vector v ~ N(0, I), each token is
+    v + 0.1 N(0, I), every row scaled to unit RMS."""
+    T = w.T if T is None else T
+    run = torch.from_numpy(run_lengths(T, 0.3, _seed(w.seed, block, "runs")))
+    n_runs = int(run.max().item()) + 1
+    base = _normal((n_runs, w.d), 1.0, "cpu", _seed(w.seed, block, "base"), torch.float32)
+    noise = _normal((T, w.d), 1.0, "cpu", _seed(w.seed, block, "noise"), torch.float32)
+    return _unit_rms_rows(base[run] + 0.1 * noise)
+
+
+def biased_rows(t: torch.Tensor, W_g: torch.Tensor, b, dt) -> torch.Tensor:
+    """Rows t moved by the folded bias u of ``fold_bias`` (float64 add on the
+    host), rounded to dt."""
+    u = fold_bias(W_g, b)
+    return (t.double() + u[None, :]).float().to(dt)
+
+
 def make_x(w: Workload, W_g: torch.Tensor, device="cpu", block: int = 0,
            T: int | None = None) -> torch.Tensor:
-    """Token rows [T, d] in the workload's dtype."""
+    """Token rows [T, d] in the workload's dtype, drawn on the host (so the
+    routing of a workload does not depend on the device) and copied to
+    ``device``."""
     T = w.T if T is None else T
     dt = w.torch_dtype
     if w.x_recipe == "normal":
-        return _normal((T, w.d), 1.0, device, _seed(w.seed, block, "x"), dt)
-    if w.x_recipe == "unit_rms":
-        t = _normal((T, w.d), 1.0, device, _seed(w.seed, block, "x"), torch.float32)
-        return _unit_rms_rows(t).to(dt)
-    if w.x_recipe == "zipf_runs":
-        run = torch.from_numpy(run_lengths(T, 0.3, _seed(w.seed, block, "runs"))).to(device)
-        n_runs = int(run.max().item()) + 1
-        base = _normal((n_runs, w.d), 1.0, device, _seed(w.seed, block, "base"), torch.float32)
-        noise = _normal((T, w.d), 1.0, device, _seed(w.seed, block, "noise"), torch.float32)
-        t = _unit_rms_rows(base[run] + 0.1 * noise)
-        if w.E == len(ZIPF_BIAS):
-            u = fold_bias(W_g, ZIPF_BIAS).to(device=device, dtype=torch.float64)
-            t = (t.double() + u[None, :]).float()
-        return t.to(dt)
-    raise ValueError("unknown x recipe " + w.x_recipe)
+        x = _normal((T, w.d), 1.0, "cpu", _seed(w.seed, block, "x"), dt)
+    elif w.x_recipe == "unit_rms":
+        t = _normal((T, w.d), 1.0, "cpu", _seed(w.seed, block, "x"), torch.float32)
+        x = _unit_rms_rows(t).to(dt)
+    elif w.x_recipe == "zipf_runs":
+        t = zipf_rows(w, block, T)
+        x = biased_rows(t, W_g, ZIPF_BIAS, dt) if w.E == len(ZIPF_BIAS) else t.to(dt)
+    else:
+        raise ValueError("unknown x recipe " + w.x_recipe)
+    return x.to(device)
 
 
 def layer_inputs(w, device="cpu", block: int = 0, T: int | None = None):
