@@ -132,6 +132,31 @@ moe_status moe_forward(const void* x, const void* W_g, const void* const* W1,
                        int32_t y_dtype, int32_t accumulate, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/*
+ * For callers that cannot allocate (code under HIP graph capture, serving
+ * loops, harnesses that forbid hipMalloc): moe_forward with its workspace
+ * taken from a static device array of MOE_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * inside the library instead of a caller's buffer.  Same arguments as
+ * moe_forward minus the workspace; same results, bit for bit.
+ *   - Each device the library runs on holds its own copy of the array until
+ *     the process ends; its address is looked up on the first call made with
+ *     that device current.  The call allocates nothing and calls no
+ *     allocating routine.
+ *   - A shape whose moe_workspace_size exceeds MOE_NOALLOC_SCRATCH_BYTES is
+ *     refused with MOE_EWORKSPACE before anything is enqueued (at Mixtral
+ *     shape, d = 4096, d_ff = 14336, E = 8, K = 2, that is above ~300 tokens).
+ *   - Every call on one device uses that device's one array, and nothing in
+ *     it needs clearing between calls (each kernel writes what a later one
+ *     reads).  Calls that overlap in time on one device (other streams, other
+ *     threads) race on it: order them, e.g. on one stream.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
+
+moe_status moe_forward_noalloc(const void* x, const void* W_g, const void* const* W1,
+                               const void* const* W3, const void* const* W2, int64_t T,
+                               int64_t d, int64_t d_ff, int32_t E, int32_t K, int32_t dtype,
+                               void* y, int32_t y_dtype, int32_t accumulate, void* stream);
+
 /* ---- the five steps, one kernel each, for callers that own the buffers ---- */
 
 /*

@@ -26,6 +26,7 @@ __all__ = [
     "moe_router_topk", "moe_route_permute", "moe_expert_swiglu", "moe_swiglu_finish",
     "moe_expert_down",
     "moe_combine", "moe_rmsnorm", "moe_stack_forward", "EXPORTED_SYMBOLS",
+    "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
     "swa_workspace_size", "swa_attention", "swa_cache_append",
 ]
 
@@ -37,8 +38,12 @@ EXPORTED_SYMBOLS = (
     "moe_status_str", "moe_last_error", "moe_abi_version", "moe_plan_for", "moe_workspace_size",
     "moe_workspace_layout", "moe_forward", "moe_router_topk", "moe_route_permute",
     "moe_expert_swiglu", "moe_swiglu_finish", "moe_expert_down", "moe_combine", "moe_rmsnorm",
-    "swa_workspace_size", "swa_attention", "swa_cache_append",
+    "swa_workspace_size", "swa_attention", "swa_cache_append", "moe_forward_noalloc",
 )
+
+# Size of the library's static scratch behind moe_forward_noalloc
+# (MOE_NOALLOC_SCRATCH_BYTES in the header).
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -87,6 +92,8 @@ def load_library(path: str | None = None):
                                           ctypes.POINTER(_c_sz)]),
         "moe_forward": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32,
                                  _c_i32, _c_i32, _c_p, _c_i32, _c_i32, _c_p, _c_sz, _c_p]),
+        "moe_forward_noalloc": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64,
+                                         _c_i32, _c_i32, _c_i32, _c_p, _c_i32, _c_i32, _c_p]),
         "moe_router_topk": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_p,
                                      _c_p, _c_p, _c_p]),
         "moe_route_permute": (_c_i32, [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p]),
@@ -217,6 +224,27 @@ def moe_forward(x, W_g, W1, W3, W2, K, y=None, y_dtype=None, accumulate=False, w
     _check(lib.moe_forward(_ptr(x), _ptr(W_g), _ptr_array(W1), _ptr_array(W3), _ptr_array(W2),
                            T, d, d_ff, E, K, dt, _ptr(y), ycode, 1 if accumulate else 0,
                            _ptr(workspace), workspace.numel(), _stream(stream)), lib)
+    return y
+
+
+def moe_forward_noalloc(x, W_g, W1, W3, W2, K, y=None, y_dtype=None, accumulate=False,
+                        stream=None):
+    """moe_forward with the library's static device scratch as workspace: the
+    call allocates nothing on the device (pass ``y`` to allocate nothing at
+    all).  Shapes whose workspace exceeds NOALLOC_SCRATCH_BYTES raise
+    MoeError (MOE_EWORKSPACE).  Calls that overlap in time on one device race
+    on the scratch."""
+    lib = load_library()
+    T, d = x.shape
+    E = len(W1)
+    d_ff = W1[0].shape[1]
+    dt = _dtype_code(x)
+    if y is None:
+        ydt = x.dtype if y_dtype is None else y_dtype
+        y = torch.empty((T, d), dtype=ydt, device=x.device)
+    _check(lib.moe_forward_noalloc(_ptr(x), _ptr(W_g), _ptr_array(W1), _ptr_array(W3),
+                                   _ptr_array(W2), T, d, d_ff, E, K, dt, _ptr(y), _dtype_code(y),
+                                   1 if accumulate else 0, _stream(stream)), lib)
     return y
 
 

@@ -431,6 +431,69 @@ moe_status moe_forward(const void* x, const void* W_g, const void* const* W1,
   return ok();
 }
 
+// ---- allocation-free variant of moe_forward ----
+
+}  // extern "C"
+
+// The scratch of moe_forward_noalloc: a device array of fixed size, one copy
+// per device the library runs on, held until the process ends.  Host code
+// never passes this name to a kernel (on the host it is only a stand-in for
+// the symbol); the device address comes from hipGetSymbolAddress, once per
+// device, and is kept in g_scratch_addr.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current.
+moe_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_EHIP, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255u))
+      return fail(MOE_EHIP, "static scratch has no 256-byte aligned device address");
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward_noalloc(const void* x, const void* W_g, const void* const* W1,
+                               const void* const* W3, const void* const* W2, int64_t T,
+                               int64_t d, int64_t d_ff, int32_t E, int32_t K, int32_t dtype,
+                               void* y, int32_t y_dtype, int32_t accumulate, void* stream) {
+  moe_status s = check_shape(T, d, d_ff, E, K, dtype);
+  if (s) return s;
+  if (T == 0)
+    return moe_forward(x, W_g, W1, W3, W2, T, d, d_ff, E, K, dtype, y, y_dtype, accumulate,
+                       nullptr, 0, stream);
+  size_t off[MOE_WS_COUNT], need;
+  layout(T, d, d_ff, E, K, dtype, off, &need);
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_EWORKSPACE,
+                "moe_forward_noalloc: this shape needs %zu bytes of scratch, the static scratch "
+                "holds %zu; call moe_forward with a workspace instead",
+                need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((s = scratch_address(&ws))) return s;
+  return moe_forward(x, W_g, W1, W3, W2, T, d, d_ff, E, K, dtype, y, y_dtype, accumulate, ws,
+                     (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 // ---- attention sub-block ----
 
 namespace {

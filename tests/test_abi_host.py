@@ -125,6 +125,27 @@ def test_forward_empty_batch_is_a_noop(lib):
     assert lib.moe_last_error() == b""
 
 
+def _noalloc(lib, T, d=4096, d_ff=14336, E=8, K=2, dtype=1):
+    ptrs = (ctypes.c_void_p * E)(*([FAKE] * E))
+    return lib.moe_forward_noalloc(FAKE, FAKE, ptrs, ptrs, ptrs, T, d, d_ff, E, K, dtype, FAKE2,
+                                   dtype, 0, None)
+
+
+def test_noalloc_scratch_limit_and_noop(lib):
+    """moe_forward_noalloc refuses, before touching the device, a shape whose
+    workspace exceeds the static scratch; the limit in the header and in the
+    binding agree; an empty batch is a no-op."""
+    text = open(HEADER).read()
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \((\d+) \* 1024 \* 1024\)", text)
+    assert m and int(m.group(1)) * 1024 * 1024 == M.NOALLOC_SCRATCH_BYTES
+    assert M.workspace_size(4096, 4096, 14336, 8, 2, M.BF16) > M.NOALLOC_SCRATCH_BYTES
+    assert M.workspace_size(8, 4096, 14336, 8, 2, M.BF16) <= M.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(lib, 4096) == EWORKSPACE
+    assert b"static scratch" in lib.moe_last_error()
+    assert _noalloc(lib, 8, d=100) == EUNSUPPORTED
+    assert _noalloc(lib, 0) == OK
+
+
 def test_stage_entry_points_validate(lib):
     arr = (ctypes.c_void_p * 8)(*([FAKE] * 8))
     assert lib.moe_router_topk(FAKE, FAKE, 4, 64, 8, 0, 1, FAKE, FAKE, None, None) == EINVAL
