@@ -186,6 +186,22 @@ moe_status moe_route_permute(const int32_t* topk_idx, int64_t T, int32_t E, int3
                              void* stream);
 
 /*
+ * Routing statistics of one layer, from the router's table ("Mixtral of
+ * Experts", xyznot.com, limitations: consecutive tokens share their
+ * first-choice expert more often than random routing's 1/E; "杀疯了的开源专家
+ * 模型 Mixtral 8x7B 论文公开啦！", redian.news, 实验: per layer, consecutive
+ * tokens are often assigned the same expert):
+ *   counts  int32 [E]: pairs (t, r) with topk_idx[t, r] = e (the load of e)
+ *   repeats int32 [1]: tokens t in 1..T-1 whose first choice equals that of
+ *           token t-1 (the first-choice repeat rate is repeats / (T - 1))
+ * topk_idx int32 [T, K] in rank order, as moe_router_topk writes it; an index
+ * outside [0, E) counts nowhere and never repeats.  Bit-exact integers.
+ * T == 0 launches nothing and leaves the outputs as they are.
+ */
+moe_status moe_routing_stats(const int32_t* topk_idx, int64_t T, int32_t E, int32_t K,
+                             int32_t* counts, int32_t* repeats, void* stream);
+
+/*
  * Step 6 (code block D, first line): for every expert-sorted pair row r of
  * expert e, H[r] = round(SiLU(x[sorted_token[r]] W1[e]) * (x[...] W3[e])),
  * fp32 accumulation, one rounding to dtype.  H [T*K, d_ff] in dtype.

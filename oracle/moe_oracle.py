@@ -57,6 +57,7 @@ __all__ = [
     "rmsnorm",
     "stack_forward",
     "routing_margins",
+    "routing_stats",
 ]
 
 
@@ -303,3 +304,27 @@ def routing_margins(logits, K: int):
         m_rank = np.full(T, np.inf)
     m_cut = s[:, K - 1] - s[:, K] if K < E else np.full(T, np.inf)
     return m_rank, m_cut
+
+
+# ---------------------------------------------------------------------------
+# Routing statistics ("Mixtral of Experts" (xyznot.com), limitations: the
+# first choice of consecutive tokens repeats more often than the 1/E of random
+# routing; "杀疯了的开源专家模型 Mixtral 8x7B 论文公开啦！" (redian.news), 实验:
+# per layer, consecutive tokens are often assigned the same expert)
+# ---------------------------------------------------------------------------
+def routing_stats(idx, E: int):
+    """(counts[E], repeats) of one layer's routing table idx [T, K]:
+    counts[e] = pairs routed to expert e; repeats = number of tokens t >= 1
+    whose first choice idx[t, 0] equals idx[t - 1, 0].  Indices outside
+    [0, E) count nowhere and never repeat."""
+    idx = np.asarray(idx)
+    T = idx.shape[0]
+    counts = np.zeros(E, dtype=np.int64)
+    for v in idx.reshape(-1):
+        if 0 <= v < E:
+            counts[v] += 1
+    repeats = 0
+    for t in range(1, T):
+        if idx[t, 0] == idx[t - 1, 0] and 0 <= idx[t, 0] < E:
+            repeats += 1
+    return counts, repeats

@@ -26,7 +26,7 @@ __all__ = [
     "moe_router_topk", "moe_route_permute", "moe_expert_swiglu", "moe_swiglu_finish",
     "moe_expert_down",
     "moe_combine", "moe_rmsnorm", "moe_stack_forward", "EXPORTED_SYMBOLS",
-    "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "moe_routing_stats",
     "swa_workspace_size", "swa_attention", "swa_cache_append",
 ]
 
@@ -39,6 +39,7 @@ EXPORTED_SYMBOLS = (
     "moe_workspace_layout", "moe_forward", "moe_router_topk", "moe_route_permute",
     "moe_expert_swiglu", "moe_swiglu_finish", "moe_expert_down", "moe_combine", "moe_rmsnorm",
     "swa_workspace_size", "swa_attention", "swa_cache_append", "moe_forward_noalloc",
+    "moe_routing_stats",
 )
 
 # Size of the library's static scratch behind moe_forward_noalloc
@@ -97,6 +98,7 @@ def load_library(path: str | None = None):
         "moe_router_topk": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_p,
                                      _c_p, _c_p, _c_p]),
         "moe_route_permute": (_c_i32, [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p]),
+        "moe_routing_stats": (_c_i32, [_c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p]),
         "moe_expert_swiglu": (_c_i32, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32,
                                        _c_i32, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
         "moe_swiglu_finish": (_c_i32, [_c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_p,
@@ -274,6 +276,22 @@ def moe_route_permute(topk_idx, E, offsets=None, sorted_token=None, pos=None, st
     _check(lib.moe_route_permute(_ptr(topk_idx), T, E, K, _ptr(offsets), _ptr(sorted_token),
                                  _ptr(pos), _stream(stream)), lib)
     return offsets, sorted_token, pos
+
+
+def moe_routing_stats(topk_idx, E, counts=None, repeats=None, stream=None):
+    """Per-expert pair counts (int32 [E]) and the number of first-choice
+    repeats between consecutive tokens (int32 [1]) of one layer's routing
+    table topk_idx [T, K]."""
+    lib = load_library()
+    T, K = topk_idx.shape
+    dev = topk_idx.device
+    if counts is None:
+        counts = torch.zeros(E, dtype=torch.int32, device=dev)
+    if repeats is None:
+        repeats = torch.zeros(1, dtype=torch.int32, device=dev)
+    _check(lib.moe_routing_stats(_ptr(topk_idx), T, E, K, _ptr(counts), _ptr(repeats),
+                                 _stream(stream)), lib)
+    return counts, repeats
 
 
 def moe_expert_swiglu(x, W1, W3, K, offsets, sorted_token, H=None, scratch=None, stream=None,

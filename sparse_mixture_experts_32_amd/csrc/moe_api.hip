@@ -242,6 +242,18 @@ moe_status moe_route_permute(const int32_t* topk_idx, int64_t T, int32_t E, int3
                     "route_permute");
 }
 
+moe_status moe_routing_stats(const int32_t* topk_idx, int64_t T, int32_t E, int32_t K,
+                             int32_t* counts, int32_t* repeats, void* stream) {
+  if (T < 0) return fail(MOE_EINVAL, "T < 0");
+  if (E < 1 || E > MOE_MAX_EXPERTS || K < 1 || K > E) return fail(MOE_EINVAL, "bad E or K");
+  if (T * (int64_t)K >= (int64_t(1) << 31)) return fail(MOE_EINVAL, "T*K must be < 2^31");
+  if (T == 0) return ok();
+  if (!topk_idx || !counts || !repeats) return fail(MOE_EINVAL, "NULL pointer");
+  return finish(moe::launch_routing_stats(topk_idx, (int)T, E, K, counts, repeats,
+                                          (hipStream_t)stream),
+                "routing_stats");
+}
+
 }  // extern "C"
 
 namespace {

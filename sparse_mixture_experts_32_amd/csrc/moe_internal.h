@@ -19,6 +19,10 @@ hipError_t launch_router_topk(const void* x, const void* Wg, int T, int d, int E
 hipError_t launch_route_permute(const int32_t* topk_idx, int T, int E, int K, int32_t* offsets,
                                 int32_t* sorted_token, int32_t* pos, hipStream_t stream);
 
+// counts[e] = pairs routed to e; repeats[0] = #{t >= 1 : idx[t][0] == idx[t-1][0]}.
+hipError_t launch_routing_stats(const int32_t* topk_idx, int T, int E, int K, int32_t* counts,
+                                int32_t* repeats, hipStream_t stream);
+
 // a6: H[r] = round(SiLU(A[r] W1[e]) * (A[r] W3[e])) over the expert-sorted
 // rows r of expert e, A[r] = x[sorted_token[r]].
 hipError_t launch_expert_swiglu_bf16(const void* x, const int32_t* sorted_token,

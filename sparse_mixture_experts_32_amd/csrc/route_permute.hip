@@ -173,7 +173,46 @@ __global__ __launch_bounds__(kPermuteThreads) void route_permute_held_kernel(
   }
 }
 
+// Routing statistics of one layer: pairs per expert and first-choice repeats
+// between consecutive tokens ("Mixtral of Experts" (xyznot.com),
+// limitations: consecutive tokens keep their first-choice expert more often
+// than the 1/E of random routing).  One workgroup; LDS integer atomics and a
+// wave sum of integers, so the counts do not depend on the order of updates.
+__global__ __launch_bounds__(kPermuteThreads) void routing_stats_kernel(
+    const int32_t* __restrict__ topk_idx, int T, int E, int K, int32_t* __restrict__ counts,
+    int32_t* __restrict__ repeats) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int rep;
+  const int tid = threadIdx.x;
+  if (tid < kMaxExperts) cnt[tid] = 0;
+  if (tid == 0) rep = 0;
+  __syncthreads();
+  const int64_t P = (int64_t)T * K;
+  for (int64_t p = tid; p < P; p += kPermuteThreads) {
+    const int e = topk_idx[p];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  int mine = 0;
+  for (int64_t t = 1 + tid; t < T; t += kPermuteThreads) {
+    const int a = topk_idx[(t - 1) * K], b = topk_idx[t * K];
+    mine += (b == a && b >= 0 && b < E) ? 1 : 0;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) mine += __shfl_xor(mine, m, 64);
+  if ((tid & 63) == 0 && mine) atomicAdd(&rep, mine);
+  __syncthreads();
+  if (tid < E) counts[tid] = cnt[tid];
+  if (tid == 0) repeats[0] = rep;
+}
+
 }  // namespace
+
+hipError_t launch_routing_stats(const int32_t* topk_idx, int T, int E, int K, int32_t* counts,
+                                int32_t* repeats, hipStream_t stream) {
+  hipLaunchKernelGGL(routing_stats_kernel, dim3(1), dim3(kPermuteThreads), 0, stream, topk_idx, T,
+                     E, K, counts, repeats);
+  return hipGetLastError();
+}
 
 hipError_t launch_route_permute(const int32_t* topk_idx, int T, int E, int K, int32_t* offsets,
                                 int32_t* sorted_token, int32_t* pos, hipStream_t stream) {

@@ -484,6 +484,39 @@ def check_margins_hand():
     assert m_rank[0] == 1.5 and m_cut[0] == 0.5
 
 
+# --- routing statistics ----------------------------------------------------------
+def check_routing_stats_hand():
+    """Hand case: first choices 0 0 1 1 1 2 0 repeat at t = 1, 3, 4 (three
+    repeats in six consecutive pairs); the second choices (1 2 2 0 2 3 3) would
+    give two (t = 2, 6).  Every pair counts towards its expert's load."""
+    idx = np.array([[0, 1], [0, 2], [1, 2], [1, 0], [1, 2], [2, 3], [0, 3]])
+    counts, repeats = O.routing_stats(idx, 4)
+    assert repeats == 3
+    assert counts.tolist() == [4, 4, 4, 2]
+    # an index outside [0, E) counts nowhere and breaks a run
+    idx2 = np.array([[0, 1], [-1, 2], [-1, 0], [0, 7]])
+    counts2, repeats2 = O.routing_stats(idx2, 4)
+    assert repeats2 == 0 and counts2.tolist() == [3, 1, 1, 0]
+    assert O.routing_stats(np.zeros((1, 2), dtype=int), 3)[1] == 0
+
+
+def check_routing_stats_random_rate():
+    """"Mixtral of Experts" (xyznot.com), limitations: random assignment
+    repeats the first choice 12.5 % of the time with 8 experts, i.e. 1/E.
+    Uniform random first choices over 200001 tokens must land within five
+    binomial standard deviations of 1/8; the loads sum to T*K."""
+    T, E, K = 200_001, 8, 2
+    r = _rng(31)
+    scores = r.random((T, E))
+    idx = np.argsort(scores, axis=1)[:, :K]
+    counts, repeats = O.routing_stats(idx, E)
+    rate = repeats / (T - 1)
+    sigma = math.sqrt((1 / E) * (1 - 1 / E) / (T - 1))
+    assert abs(rate - 1 / E) < 5 * sigma, rate
+    assert counts.sum() == T * K
+    assert np.array_equal(counts, np.bincount(idx.reshape(-1), minlength=E))
+
+
 # --- shapes -------------------------------------------------------------------
 def mixtral_param_counts(d, d_ff, E, K, layers=32, vocab=32000, n_q=32, n_kv=8, head=128):
     attn = d * n_q * head + 2 * d * n_kv * head + n_q * head * d

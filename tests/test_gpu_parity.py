@@ -243,6 +243,28 @@ def test_dropped_pairs_add_nothing(dev, T, E, K, splits):
     assert torch.all(y_drop[20] == 0)                  # both of token 20's pairs dropped
 
 
+@pytest.mark.parametrize("T,E,K", [(1, 8, 2), (2, 8, 2), (37, 4, 2), (5000, 8, 2),
+                                   (70000, 8, 1), (3000, 64, 4)])
+def test_routing_stats_bit_exact(dev, T, E, K):
+    """Expert loads and first-choice repeats of consecutive tokens, on
+    routings with planted same-expert runs and out-of-range entries."""
+    say("routing stats", T, E, K)
+    idx = random_routing(T, E, K, seed=T * 7 + E + K)
+    g = torch.Generator().manual_seed(T + 1)
+    run = torch.rand(T, generator=g) < 0.4            # token repeats its predecessor's row
+    for t in range(1, T):
+        if run[t]:
+            idx[t] = idx[t - 1]
+    if T > 3:
+        idx[T // 2, 0] = -1
+        idx[T // 3, K - 1] = E
+    counts, repeats = M.moe_routing_stats(idx.to(torch.int32).to(dev), E)
+    torch.cuda.synchronize()
+    r_counts, r_repeats = O.routing_stats(idx.numpy(), E)
+    assert counts.cpu().numpy().tolist() == r_counts.tolist()
+    assert int(repeats.item()) == r_repeats
+
+
 # ---------------------------------------------------------------- layer
 def test_layer_tiny_f32(dev):
     w = W.WORKLOADS["tiny_f32_T64"]

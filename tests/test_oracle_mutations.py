@@ -115,6 +115,27 @@ def _stack_no_residual_rounding(h0, blocks, K, eps=1e-5, faithful=False):
     return h, margins
 
 
+def _stats_second_choice(idx, E):
+    idx = np.asarray(idx)
+    counts = np.bincount(idx[(idx >= 0) & (idx < E)].reshape(-1), minlength=E)
+    col = idx[:, -1]
+    return counts, int(np.sum((col[1:] == col[:-1]) & (col[1:] >= 0) & (col[1:] < E)))
+
+
+def _stats_first_choice_load(idx, E):
+    idx = np.asarray(idx)
+    first = idx[:, 0]
+    counts = np.bincount(first[(first >= 0) & (first < E)], minlength=E)
+    return counts, int(np.sum((first[1:] == first[:-1]) & (first[1:] >= 0) & (first[1:] < E)))
+
+
+def _stats_stride_two(idx, E):
+    idx = np.asarray(idx)
+    counts = np.bincount(idx[(idx >= 0) & (idx < E)].reshape(-1), minlength=E)
+    first = idx[:, 0]
+    return counts, int(np.sum((first[2:] == first[:-2]) & (first[2:] >= 0) & (first[2:] < E)))
+
+
 _orig_swiglu = O.swiglu_expert
 _orig_route = O.route_tables
 _orig_gate_weights = O.gate_weights
@@ -134,6 +155,9 @@ MUTATIONS = {
     "stack_post_norm": ("stack_forward", _stack_post_norm),
     "stack_every_block_reads_h0": ("stack_forward", _stack_blocks_read_h0),
     "stack_faithful_skips_residual_rounding": ("stack_forward", _stack_no_residual_rounding),
+    "stats_repeat_on_second_choice": ("routing_stats", _stats_second_choice),
+    "stats_load_counts_first_choice_only": ("routing_stats", _stats_first_choice_load),
+    "stats_compares_tokens_two_apart": ("routing_stats", _stats_stride_two),
 }
 
 

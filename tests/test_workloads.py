@@ -49,3 +49,18 @@ def test_prefill_recipe_routing_structure():
     first = idx[:, 0]
     repeat = np.mean(first[1:] == first[:-1])
     assert repeat > 0.5            # runs of shared base vectors
+
+
+def test_uniform_recipe_first_choice_repeat_rate():
+    """The 512-token workload routes near-uniformly: its consecutive tokens
+    repeat their first choice at about random routing's 1/E = 12.5 %
+    ("Mixtral of Experts" (xyznot.com), limitations), within three binomial
+    standard deviations (routing by the oracle's float64 router)."""
+    w = W.WORKLOADS["mid_bf16_T512"]
+    W_g, _, _, _ = W.expert_weights(w, experts=[])
+    x = W.make_x(w, W_g)
+    idx = O.topk_select(O.router_logits(x.float().numpy(), W_g.float().numpy()), w.K)
+    _, repeats = O.routing_stats(idx, w.E)
+    rate = repeats / (w.T - 1)
+    sigma = np.sqrt(0.125 * 0.875 / (w.T - 1))
+    assert abs(rate - 0.125) < 3 * sigma, rate
