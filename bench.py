@@ -548,12 +548,11 @@ def run_stacks(dev, steps, warmup, decode_steps):
     for T in (w.T, DECODE_STACK_T):
         h0 = W.make_x(w, blocks[0][0], dev, T=T)
         h = h0.clone()
-        ws = torch.empty(M.workspace_size(T, w.d, w.d_ff, w.E, w.K, M.BF16), dtype=torch.uint8,
-                         device=dev)
-        xn = torch.empty_like(h)
+        ws = torch.empty(M.stack_workspace_size(T, w.d, w.d_ff, w.E, w.K, M.BF16),
+                         dtype=torch.uint8, device=dev)
 
         def run():
-            M.moe_stack_forward(h, blocks, w.K, workspace=ws, xn=xn)
+            M.moe_stack_forward(h, blocks, w.K, workspace=ws)
 
         t = _time_stack(h, h0, run, steps if T == w.T else decode_steps, warmup)
         n = steps if T == w.T else decode_steps
@@ -561,18 +560,21 @@ def run_stacks(dev, steps, warmup, decode_steps):
         res = dict(workload="stack32_bf16_T%d" % T, T=T, layers=w.layers, steps=n,
                    ms_per_step=round(ms, 3), tokens_per_s=round(T / (ms * 1e-3), 1),
                    weights_gb=round(weights_gb, 1))
+        # routing statistics of every block (untimed pass): expert loads and
+        # the first-choice repeat rate of consecutive tokens, from the kernels
+        stats = torch.empty((w.layers, w.E + 1), dtype=torch.int32, device=dev)
+        h.copy_(h0)
+        M.moe_stack_forward(h, blocks, w.K, workspace=ws, stats=stats)
+        st = stats.cpu().numpy()
+        n_active = [int(np.sum(row[:w.E] > 0)) for row in st]
+        res["layer_expert_counts"] = st[:, :w.E].tolist()
+        res["layer_first_choice_repeat_rate"] = [round(float(r) / max(T - 1, 1), 4)
+                                                 for r in st[:, w.E]]
         if T == w.T:
             flops = w.layers * (T * w.K * 6 * w.d * w.d_ff)
             res["achieved_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
             res["mfma_frac"] = round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
         else:
-            # experts that received tokens, block by block (untimed pass)
-            views = M.workspace_views(ws, T, w.d, w.d_ff, w.E, w.K, M.BF16)
-            h.copy_(h0)
-            n_active = []
-            for blk in blocks:
-                M.moe_stack_forward(h, [blk], w.K, workspace=ws, xn=xn)
-                n_active.append(int((views["offsets"].diff() > 0).sum().item()))
             alg = sum(n_active) * 3 * w.d * w.d_ff * 2 + w.layers * (
                 w.d * w.E * 2 + 3 * T * w.d * 2)
             res["n_active_per_block"] = n_active
@@ -592,7 +594,7 @@ def run_stacks(dev, steps, warmup, decode_steps):
             res["graph_hbm_frac"] = round(alg / (HBM_PEAK_GBS * 1e9) / (msg * 1e-3), 4)
             del g
         out.append(res)
-        del h, h0, ws, xn
+        del h, h0, ws
     del blocks
     torch.cuda.empty_cache()
     return out
@@ -625,6 +627,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps(dict(copy_bytes_read=n, copy_bytes_written=n, calls=args.steps)))
+        return
+    if args.only == "stack":
+        print(json.dumps(run_stacks(dev, 3, 1, 10)), flush=True)
         return
     if args.only == "attention":
         print(json.dumps(run_attention(dev, args.steps, args.warmup, cpu=False)), flush=True)

@@ -248,6 +248,38 @@ moe_status moe_combine(const float* O, int32_t o_splits, const float* topk_w, co
                        int32_t accumulate, void* stream);
 
 /*
+ * Bytes of workspace moe_stack_forward needs: one layer's intermediates
+ * (moe_workspace_layout) followed by the normalised block input [T, d].
+ */
+moe_status moe_stack_workspace_size(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K,
+                                    int32_t dtype, size_t* bytes);
+
+/*
+ * A stack of L pre-norm blocks ("【DL輪読会】Mixtral of Experts" slides,
+ * "Architecture – 全体": RMSNorm, then the mixture of experts, then the
+ * residual add), in place on h [T, d]:
+ *     for l = 0 .. L-1:   h = round(h + MoE_l(RMSNorm(h)))
+ * with RMSNorm(h) = round(h / sqrt(mean(h^2) + eps)), unit gain.
+ *   W_g   host array of L device pointers, block l's router [d, E]
+ *   W1, W3, W2  host arrays of L*E device pointers; block l, expert e at
+ *         index l*E + e (shapes as in moe_forward)
+ *   stats NULL, or device int32 [L][E + 1]: block l's expert loads and then
+ *         its first-choice repeats (what moe_routing_stats writes for it)
+ *   workspace  moe_stack_workspace_size bytes, 256-byte aligned, not
+ *         overlapping h
+ * The result is that of moe_rmsnorm followed by moe_forward(accumulate = 1)
+ * for each block in turn, bit for bit.  For small batches (the streaming
+ * plan) one launch joins consecutive blocks: the previous block's combine
+ * with the residual add, the RMSNorm and the next block's router.  Same
+ * limits and errors as moe_forward; L = 0 or T = 0 is a no-op.
+ */
+moe_status moe_stack_forward(void* h, const void* const* W_g, const void* const* W1,
+                             const void* const* W3, const void* const* W2, int32_t L, int64_t T,
+                             int64_t d, int64_t d_ff, int32_t E, int32_t K, float eps,
+                             int32_t dtype, int32_t* stats, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * Pre-norm glue for a stack of blocks ("【DL輪読会】Mixtral of Experts"
  * slides, "Architecture – 全体": RMSNorm before the MoE block):
  * out[t] = round(h[t] / sqrt(mean(h[t]^2) + eps)), unit gain, fp32 math.

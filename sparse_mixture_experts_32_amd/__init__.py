@@ -27,6 +27,7 @@ __all__ = [
     "moe_expert_down",
     "moe_combine", "moe_rmsnorm", "moe_stack_forward", "EXPORTED_SYMBOLS",
     "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "moe_routing_stats",
+    "stack_workspace_size",
     "swa_workspace_size", "swa_attention", "swa_cache_append",
 ]
 
@@ -39,7 +40,7 @@ EXPORTED_SYMBOLS = (
     "moe_workspace_layout", "moe_forward", "moe_router_topk", "moe_route_permute",
     "moe_expert_swiglu", "moe_swiglu_finish", "moe_expert_down", "moe_combine", "moe_rmsnorm",
     "swa_workspace_size", "swa_attention", "swa_cache_append", "moe_forward_noalloc",
-    "moe_routing_stats",
+    "moe_routing_stats", "moe_stack_workspace_size", "moe_stack_forward",
 )
 
 # Size of the library's static scratch behind moe_forward_noalloc
@@ -108,6 +109,11 @@ def load_library(path: str | None = None):
         "moe_combine": (_c_i32, [_c_p, _c_i32, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_i32,
                                  _c_i32, _c_p]),
         "moe_rmsnorm": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, ctypes.c_float, _c_i32, _c_p]),
+        "moe_stack_workspace_size": (_c_i32, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
+                                              ctypes.POINTER(_c_sz)]),
+        "moe_stack_forward": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i64, _c_i64,
+                                       _c_i64, _c_i32, _c_i32, ctypes.c_float, _c_i32, _c_p, _c_p,
+                                       _c_sz, _c_p]),
         "swa_workspace_size": (_c_i32, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
                                         ctypes.POINTER(_c_sz)]),
         "swa_attention": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64,
@@ -362,25 +368,40 @@ def moe_rmsnorm(h, out=None, eps=1e-5, stream=None):
     return out
 
 
-def moe_stack_forward(h, blocks, K, eps=1e-5, workspace=None, xn=None, stream=None):
-    """A stack of pre-norm MoE blocks, h <- h + MoE_l(RMSNorm(h)) for every
-    block l, in place on h, through moe_rmsnorm and moe_forward(accumulate=1)
+def stack_workspace_size(T, d, d_ff, E, K, dtype) -> int:
+    lib = load_library()
+    out = _c_sz(0)
+    _check(lib.moe_stack_workspace_size(T, d, d_ff, E, K, dtype, ctypes.byref(out)), lib)
+    return out.value
+
+
+def moe_stack_forward(h, blocks, K, eps=1e-5, workspace=None, stats=None, stream=None):
+    """A stack of pre-norm MoE blocks, h <- round(h + MoE_l(RMSNorm(h))) for
+    every block l, in place on h, in one library call
     ("【DL輪読会】Mixtral of Experts" slides, "Architecture – 全体").
-    ``blocks`` is a sequence of (W_g, W1s, W3s, W2s).  Returns h."""
+    ``blocks`` is a sequence of (W_g, W1s, W3s, W2s).  ``stats``, if given, is
+    an int32 device tensor [L, E + 1] that receives every block's expert loads
+    and first-choice repeats.  Returns h."""
+    lib = load_library()
     T, d = h.shape
-    if not blocks:
+    L = len(blocks)
+    if L == 0:
         return h
     E = len(blocks[0][1])
     d_ff = blocks[0][1][0].shape[1]
+    dt = _dtype_code(h)
     if workspace is None:
-        workspace = torch.empty(max(workspace_size(T, d, d_ff, E, K, _dtype_code(h)), 1),
+        workspace = torch.empty(max(stack_workspace_size(T, d, d_ff, E, K, dt), 1),
                                 dtype=torch.uint8, device=h.device)
-    if xn is None:
-        xn = torch.empty_like(h)
-    for (W_g, W1s, W3s, W2s) in blocks:
-        moe_rmsnorm(h, xn, eps=eps, stream=stream)
-        moe_forward(xn, W_g, W1s, W3s, W2s, K, y=h, accumulate=True, workspace=workspace,
-                    stream=stream)
+    if stats is not None and (stats.dtype != torch.int32 or stats.numel() != L * (E + 1)):
+        raise ValueError("stats must be int32 with L * (E + 1) elements")
+    W_g = _ptr_array([b[0] for b in blocks])
+    W1 = _ptr_array([t for b in blocks for t in b[1]])
+    W3 = _ptr_array([t for b in blocks for t in b[2]])
+    W2 = _ptr_array([t for b in blocks for t in b[3]])
+    _check(lib.moe_stack_forward(_ptr(h), W_g, W1, W3, W2, L, T, d, d_ff, E, K,
+                                 ctypes.c_float(eps), dt, _ptr(stats), _ptr(workspace),
+                                 workspace.numel(), _stream(stream)), lib)
     return h
 
 

@@ -283,6 +283,65 @@ hipError_t run_down(const Plan& plan, const void* H, const moe::ExpertPtrs& p2,
   return moe::launch_expert_down_bf16(H, p2, offsets, P, d, d_ff, E, O, st);
 }
 
+// Intermediates of one layer inside a workspace laid out by layout().
+struct Bufs {
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* offsets;
+  int32_t* sorted_token;
+  int32_t* pos;
+  void* H;
+  float* O;
+  void* scratch;
+};
+
+Bufs carve(void* workspace, const size_t off[MOE_WS_COUNT]) {
+  char* ws = static_cast<char*>(workspace);
+  Bufs b;
+  b.topk_idx = reinterpret_cast<int32_t*>(ws + off[MOE_WS_TOPK_IDX]);
+  b.topk_w = reinterpret_cast<float*>(ws + off[MOE_WS_TOPK_W]);
+  b.offsets = reinterpret_cast<int32_t*>(ws + off[MOE_WS_OFFSETS]);
+  b.sorted_token = reinterpret_cast<int32_t*>(ws + off[MOE_WS_SORTED_TOKEN]);
+  b.pos = reinterpret_cast<int32_t*>(ws + off[MOE_WS_POS]);
+  b.H = ws + off[MOE_WS_H];
+  b.O = reinterpret_cast<float*>(ws + off[MOE_WS_O]);
+  b.scratch = ws + off[MOE_WS_SCRATCH];
+  return b;
+}
+
+// The stack's workspace: one layer's intermediates, then the normalised block
+// input xn [T, d] at *xn_off.  Returns the total size.
+size_t stack_layout(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K, int32_t dt,
+                    size_t off[MOE_WS_COUNT], size_t* xn_off) {
+  size_t total;
+  layout(T, d, d_ff, E, K, dt, off, &total);
+  *xn_off = total;
+  return align256(total + (size_t)T * d * dtype_bytes(dt));
+}
+
+// Dispatch tables, the W1/W3 product (+ finish) and the W2 product of one
+// layer whose router has filled b.topk_idx.
+moe_status run_experts(const Plan& plan, const void* x, const moe::ExpertPtrs& p1,
+                       const moe::ExpertPtrs& p3, const moe::ExpertPtrs& p2, const Bufs& b,
+                       int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K, int32_t dtype,
+                       hipStream_t st) {
+  const int P = (int)(T * K);
+  hipError_t e = moe::launch_route_permute(b.topk_idx, (int)T, E, K, b.offsets, b.sorted_token,
+                                           b.pos, st);
+  if (e != hipSuccess) return hip_status(e, "route_permute");
+  e = run_swiglu(plan, x, b.sorted_token, p1, p3, b.offsets, P, (int)d, (int)d_ff, E, dtype, b.H,
+                 b.scratch, st);
+  if (e != hipSuccess) return hip_status(e, "expert_swiglu");
+  if (plan.swiglu_splits > 0) {
+    e = moe::launch_swiglu_finish_bf16(static_cast<const float*>(b.scratch), plan.swiglu_splits,
+                                       P, (int)d_ff, b.H, st);
+    if (e != hipSuccess) return hip_status(e, "swiglu_finish");
+  }
+  e = run_down(plan, b.H, p2, b.offsets, P, (int)d, (int)d_ff, E, dtype, b.O, st);
+  if (e != hipSuccess) return hip_status(e, "expert_down");
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -409,37 +468,99 @@ moe_status moe_forward(const void* x, const void* W_g, const void* const* W1,
   if (overlap(workspace, need, x, xbytes) || overlap(workspace, need, y, ybytes))
     return fail(MOE_EINVAL, "workspace overlaps x or y");
 
-  char* ws = static_cast<char*>(workspace);
-  int32_t* topk_idx = reinterpret_cast<int32_t*>(ws + off[MOE_WS_TOPK_IDX]);
-  float* topk_w = reinterpret_cast<float*>(ws + off[MOE_WS_TOPK_W]);
-  int32_t* offsets = reinterpret_cast<int32_t*>(ws + off[MOE_WS_OFFSETS]);
-  int32_t* sorted_token = reinterpret_cast<int32_t*>(ws + off[MOE_WS_SORTED_TOKEN]);
-  int32_t* pos = reinterpret_cast<int32_t*>(ws + off[MOE_WS_POS]);
-  void* H = ws + off[MOE_WS_H];
-  float* O = reinterpret_cast<float*>(ws + off[MOE_WS_O]);
-  void* scratch = ws + off[MOE_WS_SCRATCH];
+  const Bufs b = carve(workspace, off);
   hipStream_t st = (hipStream_t)stream;
-  const int P = (int)(T * K);
   const Plan plan = make_plan(T, d, d_ff, E, K, dtype);
-
-  hipError_t e = moe::launch_router_topk(x, W_g, (int)T, (int)d, E, K, dtype, topk_idx, topk_w,
-                                         nullptr, st);
+  hipError_t e = moe::launch_router_topk(x, W_g, (int)T, (int)d, E, K, dtype, b.topk_idx,
+                                         b.topk_w, nullptr, st);
   if (e != hipSuccess) return hip_status(e, "router_topk");
-  e = moe::launch_route_permute(topk_idx, (int)T, E, K, offsets, sorted_token, pos, st);
-  if (e != hipSuccess) return hip_status(e, "route_permute");
-  e = run_swiglu(plan, x, sorted_token, p1, p3, offsets, P, (int)d, (int)d_ff, E, dtype, H,
-                 scratch, st);
-  if (e != hipSuccess) return hip_status(e, "expert_swiglu");
-  if (plan.swiglu_splits > 0) {
-    e = moe::launch_swiglu_finish_bf16(static_cast<const float*>(scratch), plan.swiglu_splits, P,
-                                       (int)d_ff, H, st);
-    if (e != hipSuccess) return hip_status(e, "swiglu_finish");
-  }
-  e = run_down(plan, H, p2, offsets, P, (int)d, (int)d_ff, E, dtype, O, st);
-  if (e != hipSuccess) return hip_status(e, "expert_down");
-  e = moe::launch_combine(O, plan.down_splits, (int64_t)P * d, topk_w, pos, (int)T, (int)d, K, y,
+  if ((s = run_experts(plan, x, p1, p3, p2, b, T, d, d_ff, E, K, dtype, st))) return s;
+  e = moe::launch_combine(b.O, plan.down_splits, T * K * d, b.topk_w, b.pos, (int)T, (int)d, K, y,
                           y_dtype, accumulate ? 1 : 0, st);
   if (e != hipSuccess) return hip_status(e, "combine");
+  return ok();
+}
+
+moe_status moe_stack_workspace_size(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K,
+                                    int32_t dtype, size_t* bytes) {
+  if (!bytes) return fail(MOE_EINVAL, "bytes is NULL");
+  moe_status s = check_shape(T, d, d_ff, E, K, dtype);
+  if (s) return s;
+  size_t off[MOE_WS_COUNT], xn_off;
+  *bytes = stack_layout(T, d, d_ff, E, K, dtype, off, &xn_off);
+  return ok();
+}
+
+moe_status moe_stack_forward(void* h, const void* const* W_g, const void* const* W1,
+                             const void* const* W3, const void* const* W2, int32_t L, int64_t T,
+                             int64_t d, int64_t d_ff, int32_t E, int32_t K, float eps,
+                             int32_t dtype, int32_t* stats, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  moe_status s = check_shape(T, d, d_ff, E, K, dtype);
+  if (s) return s;
+  if (L < 0) return fail(MOE_EINVAL, "L = %d < 0", L);
+  if (!(eps >= 0.0f)) return fail(MOE_EINVAL, "eps must be >= 0");
+  if (T == 0 || L == 0) return ok();
+  if (!h || !W_g || !W1 || !W3 || !W2) return fail(MOE_EINVAL, "NULL pointer");
+  const bool bf16 = dtype == MOE_BF16;
+  if (bf16 && !aligned16(h)) return fail(MOE_EUNSUPPORTED, "h must be 16-byte aligned");
+  for (int l = 0; l < L; ++l) {
+    if (!W_g[l]) return fail(MOE_EINVAL, "W_g[%d] is NULL", l);
+    moe::ExpertPtrs p;
+    if ((s = fill_ptrs(W1 + (size_t)l * E, E, p, "W1", bf16))) return s;
+    if ((s = fill_ptrs(W3 + (size_t)l * E, E, p, "W3", bf16))) return s;
+    if ((s = fill_ptrs(W2 + (size_t)l * E, E, p, "W2", bf16))) return s;
+  }
+  size_t off[MOE_WS_COUNT], xn_off;
+  const size_t need = stack_layout(T, d, d_ff, E, K, dtype, off, &xn_off);
+  if (!workspace) return fail(MOE_EWORKSPACE, "workspace is NULL");
+  if (workspace_bytes < need)
+    return fail(MOE_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MOE_EWORKSPACE, "workspace must be 256-byte aligned");
+  const size_t hbytes = (size_t)T * d * dtype_bytes(dtype);
+  if (overlap(workspace, need, h, hbytes)) return fail(MOE_EINVAL, "workspace overlaps h");
+  if (stats && overlap(stats, (size_t)L * (E + 1) * 4, h, hbytes))
+    return fail(MOE_EINVAL, "stats overlaps h");
+
+  const Bufs b = carve(workspace, off);
+  void* xn = static_cast<char*>(workspace) + xn_off;
+  hipStream_t st = (hipStream_t)stream;
+  const Plan plan = make_plan(T, d, d_ff, E, K, dtype);
+  const int64_t slice = T * K * d;
+  // Small batches join the blocks with one glue launch (the previous block's
+  // combine, RMSNorm, this block's router); otherwise RMSNorm, router and
+  // combine are launched one by one.  Both run the same arithmetic.
+  const bool glue = plan.streaming && moe::stack_glue_supported((int)T, (int)d, E, dtype);
+  hipError_t e = hipSuccess;
+  for (int l = 0; l < L; ++l) {
+    moe::ExpertPtrs p1, p3, p2;
+    fill_ptrs(W1 + (size_t)l * E, E, p1, "W1", bf16);
+    fill_ptrs(W3 + (size_t)l * E, E, p3, "W3", bf16);
+    fill_ptrs(W2 + (size_t)l * E, E, p2, "W2", bf16);
+    if (glue) {
+      e = moe::launch_stack_glue(h, xn, l > 0 ? b.O : nullptr, plan.down_splits, slice, b.topk_w,
+                                 b.pos, b.topk_idx, W_g[l], (int)T, (int)d, E, K, eps, st);
+      if (e != hipSuccess) return hip_status(e, "stack_glue");
+    } else {
+      e = moe::launch_rmsnorm(h, xn, (int)T, (int)d, eps, dtype, st);
+      if (e != hipSuccess) return hip_status(e, "rmsnorm");
+      e = moe::launch_router_topk(xn, W_g[l], (int)T, (int)d, E, K, dtype, b.topk_idx, b.topk_w,
+                                  nullptr, st);
+      if (e != hipSuccess) return hip_status(e, "router_topk");
+    }
+    if (stats) {
+      int32_t* sl = stats + (size_t)l * (E + 1);
+      e = moe::launch_routing_stats(b.topk_idx, (int)T, E, K, sl, sl + E, st);
+      if (e != hipSuccess) return hip_status(e, "routing_stats");
+    }
+    if ((s = run_experts(plan, xn, p1, p3, p2, b, T, d, d_ff, E, K, dtype, st))) return s;
+    if (!glue || l == L - 1) {
+      e = moe::launch_combine(b.O, plan.down_splits, slice, b.topk_w, b.pos, (int)T, (int)d, K, h,
+                              dtype, 1, st);
+      if (e != hipSuccess) return hip_status(e, "combine");
+    }
+  }
   return ok();
 }
 

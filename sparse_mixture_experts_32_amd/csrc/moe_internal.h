@@ -16,6 +16,17 @@ hipError_t launch_router_topk(const void* x, const void* Wg, int T, int d, int E
                               int dtype, int32_t* topk_idx, float* topk_w, float* logits,
                               hipStream_t stream);
 
+// Glue between pre-norm blocks for small batches (one workgroup per token):
+// [the previous block's combine into h with the residual add, when O is not
+// null], RMSNorm of h into xn, and the router of the next block on xn.
+// Bit-identical to launch_combine(accumulate) + launch_rmsnorm +
+// launch_router_topk.  Needs stack_glue_supported().
+constexpr int kStackGlueMaxD = 16384;
+bool stack_glue_supported(int T, int d, int E, int dtype);
+hipError_t launch_stack_glue(void* h, void* xn, const float* O, int o_splits, int64_t slice,
+                             float* topk_w, const int32_t* pos, int32_t* topk_idx, const void* Wg,
+                             int T, int d, int E, int K, float eps, hipStream_t stream);
+
 hipError_t launch_route_permute(const int32_t* topk_idx, int T, int E, int K, int32_t* offsets,
                                 int32_t* sorted_token, int32_t* pos, hipStream_t stream);
 

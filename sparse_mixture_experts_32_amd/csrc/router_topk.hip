@@ -69,6 +69,61 @@ __device__ __forceinline__ void bf16x8_to_f32(const uint4& v, float f[8]) {
   f[7] = __uint_as_float(v.w & 0xffff0000u);
 }
 
+// Partial logits of experts e0 .. e0+7 of one token, vector path (bf16,
+// E % 8 == 0, d % 8 == 0): the thread `sub` of the token's TPT threads takes
+// the 8-wide chunks k0 = 8 sub, 8 sub + 8 TPT, ...; a chunk is one 16-byte
+// load of x and eight 16-byte loads of the matching W_g rows.  xr may point
+// to global memory or to LDS.
+template <int TPT>
+__device__ __forceinline__ void vec_partials(const bf16_t* xr, const bf16_t* __restrict__ Wg,
+                                             int d, int E, int e0, int sub, float (&acc)[8]) {
+#pragma unroll 4
+  for (int k0 = sub * 8; k0 < d; k0 += TPT * 8) {
+    float xv[8];
+    bf16x8_to_f32(*reinterpret_cast<const uint4*>(xr + k0), xv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float wv[8];
+      bf16x8_to_f32(*reinterpret_cast<const uint4*>(Wg + (int64_t)(k0 + i) * E + e0), wv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(xv[i], wv[j], acc[j]);
+    }
+  }
+}
+
+// Top-K of one token whose logit e sits in lane e of the calling wavefront
+// (lanes >= E hold nothing): K rounds of a wave arg-max with key
+// (-logit, index); lane 0 writes rank r as soon as it is known (the weight
+// first unnormalised, divided by the total afterwards).
+__device__ __forceinline__ void select_topk(float my_logit, int lane, int E, int K,
+                                            int32_t* out_idx, float* out_w) {
+  bool taken = false;
+  float first = 0.0f, denom = 0.0f;
+  for (int r = 0; r < K; ++r) {
+    float v = my_logit;
+    int i = (lane < E && !taken) ? lane : -1;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float ov = __shfl_xor(v, m, 64);
+      const int oi = __shfl_xor(i, m, 64);
+      if (ranks_before(ov, oi, v, i)) {
+        v = ov;
+        i = oi;
+      }
+    }
+    if (lane == i) taken = true;
+    if (r == 0) first = v;
+    const float ex = expf(v - first);
+    denom += ex;
+    if (lane == 0) {
+      out_idx[r] = i;
+      out_w[r] = ex;
+    }
+  }
+  if (lane == 0)
+    for (int r = 0; r < K; ++r) out_w[r] = out_w[r] / denom;
+}
+
 template <typename T, int TPT, bool VEC>
 __global__ __launch_bounds__(256) void router_topk_kernel(const T* __restrict__ x,
                                                           const T* __restrict__ Wg, int T_,
@@ -95,18 +150,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const T* __restrict__ 
     for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
     if (live) {
       if constexpr (VEC) {
-#pragma unroll 4
-        for (int k0 = sub * 8; k0 < d; k0 += TPT * 8) {
-          float xv[8];
-          bf16x8_to_f32(*reinterpret_cast<const uint4*>(xr + k0), xv);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            float wv[8];
-            bf16x8_to_f32(*reinterpret_cast<const uint4*>(Wg + (int64_t)(k0 + i) * E + e0), wv);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] = fmaf(xv[i], wv[j], acc[j]);
-          }
-        }
+        vec_partials<TPT>(reinterpret_cast<const bf16_t*>(xr), reinterpret_cast<const bf16_t*>(Wg),
+                          d, E, e0, sub, acc);
       } else {
         for (int k = sub; k < d; k += TPT) {
           const float xv = load_f(xr, k);
@@ -132,35 +177,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const T* __restrict__ 
   const float my_logit = lane < E ? logit_sh[tok_local][lane] : 0.0f;
   if (logits_out && lane < E) logits_out[static_cast<int64_t>(t) * E + lane] = my_logit;
 
-  // K rounds of wave arg-max; lane 0 writes rank r as soon as it is known
-  // (the weight first unnormalised, divided by the total afterwards).
-  bool taken = false;
-  float first = 0.0f, denom = 0.0f;
-  int32_t* out_idx = topk_idx + static_cast<int64_t>(t) * K;
-  float* out_w = topk_w + static_cast<int64_t>(t) * K;
-  for (int r = 0; r < K; ++r) {
-    float v = my_logit;
-    int i = (lane < E && !taken) ? lane : -1;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = __shfl_xor(v, m, 64);
-      const int oi = __shfl_xor(i, m, 64);
-      if (ranks_before(ov, oi, v, i)) {
-        v = ov;
-        i = oi;
-      }
-    }
-    if (lane == i) taken = true;
-    if (r == 0) first = v;
-    const float ex = expf(v - first);
-    denom += ex;
-    if (lane == 0) {
-      out_idx[r] = i;
-      out_w[r] = ex;
-    }
-  }
-  if (lane == 0)
-    for (int r = 0; r < K; ++r) out_w[r] = out_w[r] / denom;
+  select_topk(my_logit, lane, E, K, topk_idx + static_cast<int64_t>(t) * K,
+              topk_w + static_cast<int64_t>(t) * K);
 }
 
 // Many tokens, 8 experts, bf16: a workgroup takes 4 tokens, so every
@@ -268,6 +286,216 @@ __global__ __launch_bounds__(256) void router_e8_kernel(const bf16_t* __restrict
     for (int r = 0; r < K; ++r) topk_w[t * K + r] = topk_w[t * K + r] / denom;
 }
 
+// Glue between two pre-norm blocks of a stack, for small batches (one
+// workgroup of 512 threads per token), bf16, E % 8 == 0, d % 8 == 0.  In one
+// launch, for token t:
+//   1. (COMBINE) the previous block's combine with the residual add, one
+//      thread per 4 features: s = w0 O[pos0] + ... in rank order (O summed
+//      over its slices in slice order), h[t] = round(h[t] + s) -- the
+//      arithmetic of the combine kernel;
+//   2. RMSNorm ("【DL輪読会】Mixtral of Experts" slides, "Architecture –
+//      全体"): thread i < 256 sums the squares of features i, i + 256, ... in
+//      order (read back from LDS), then a fixed tree over those 256 sums,
+//      xn = round(h / sqrt(mean + eps)) -- the arithmetic of the RMSNorm
+//      kernel;
+//   3. the next block's router on xn, held in LDS, by the first four
+//      wavefronts -- the arithmetic of the router kernel with four
+//      wavefronts per token.  Their first W_g rows are loaded at the start of
+//      the kernel, so those loads overlap steps 1 and 2.
+// The results are those of the three separate kernels, bit for bit.  Token
+// t's previous gate weights and positions are read in step 1, before the
+// barriers after which wave 0 overwrites them with the new ones, and by the
+// workgroup of token t only.
+constexpr int kGlueThreads = 512;
+constexpr int kGluePrefetch = 2;     // 8-row W_g chunks held per router thread
+constexpr int kGlueRanks = 2;        // the combine's loads are all issued at once for
+constexpr int kGlueSlices = 4;       // K <= kGlueRanks and splits <= kGlueSlices
+
+template <bool COMBINE>
+__global__ __launch_bounds__(kGlueThreads) void stack_glue_kernel(
+    bf16_t* __restrict__ h, bf16_t* __restrict__ xn, const float* __restrict__ O, int splits,
+    int64_t slice, float* __restrict__ topk_w, const int32_t* __restrict__ pos,
+    int32_t* __restrict__ topk_idx, const bf16_t* __restrict__ Wg, int d, int E, int K,
+    float eps) {
+  extern __shared__ __align__(16) bf16_t xs[];   // [d]: the new h, then xn
+  __shared__ float part[256];
+  __shared__ float wave_part[4][kMaxExperts];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t t = blockIdx.x;
+  const bool router = tid < 256;
+
+  // W_g rows of the router threads' first chunks (experts 0..7)
+  uint4 wpre[kGluePrefetch][8];
+#pragma unroll
+  for (int q = 0; q < kGluePrefetch; ++q) {
+    const int k0 = tid * 8 + q * 256 * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      wpre[q][i] = (router && k0 < d) ? *reinterpret_cast<const uint4*>(Wg + (int64_t)(k0 + i) * E)
+                                      : make_uint4(0, 0, 0, 0);
+  }
+
+  bf16_t* hr = h + t * d;
+  if constexpr (COMBINE) {
+    const float* wt = topk_w + t * K;
+    const int32_t* pt = pos + t * K;
+    // h[c..c+3] = round(h + s) from the rank sums o_r (slices added in slice
+    // order): s = w0 o_0, then s = fma(w_r, o_r, s) in rank order
+    auto store = [&](int c, uint2 hv, float s0, float s1, float s2, float s3) {
+      uint2 out;
+      out.x = pack_bf16x2(__uint_as_float(hv.x << 16) + s0, __uint_as_float(hv.x & 0xffff0000u) + s1);
+      out.y = pack_bf16x2(__uint_as_float(hv.y << 16) + s2, __uint_as_float(hv.y & 0xffff0000u) + s3);
+      *reinterpret_cast<uint2*>(hr + c) = out;
+      *reinterpret_cast<uint2*>(xs + c) = out;
+    };
+    auto o_row = [&](int r, int sl, int c) {
+      const int p = pt[r];
+      if (p < 0) return make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      return *reinterpret_cast<const float4*>(O + sl * slice + (int64_t)p * d + c);
+    };
+    if (K <= kGlueRanks && splits <= kGlueSlices) {
+      // every load of the thread's two groups issued before any is used
+      for (int c0 = tid * 4; c0 < d; c0 += 2 * kGlueThreads * 4) {
+        float4 buf[2][kGlueRanks][kGlueSlices];
+        uint2 hv[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int c = c0 + g * kGlueThreads * 4;
+          const bool live = c < d;
+          hv[g] = live ? *reinterpret_cast<const uint2*>(hr + c) : make_uint2(0, 0);
+#pragma unroll
+          for (int r = 0; r < kGlueRanks; ++r)
+#pragma unroll
+            for (int sl = 0; sl < kGlueSlices; ++sl)
+              buf[g][r][sl] = (live && r < K && sl < splits) ? o_row(r, sl, c)
+                                                             : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int c = c0 + g * kGlueThreads * 4;
+          if (c >= d) continue;
+          float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+          for (int r = 0; r < kGlueRanks; ++r) {
+            if (r >= K) break;
+            float4 o = buf[g][r][0];
+#pragma unroll
+            for (int sl = 1; sl < kGlueSlices; ++sl) {
+              if (sl >= splits) break;
+              o.x += buf[g][r][sl].x;
+              o.y += buf[g][r][sl].y;
+              o.z += buf[g][r][sl].z;
+              o.w += buf[g][r][sl].w;
+            }
+            const float wr = wt[r];
+            if (r == 0) {
+              s0 = wr * o.x, s1 = wr * o.y, s2 = wr * o.z, s3 = wr * o.w;
+            } else {
+              s0 = fmaf(wr, o.x, s0);
+              s1 = fmaf(wr, o.y, s1);
+              s2 = fmaf(wr, o.z, s2);
+              s3 = fmaf(wr, o.w, s3);
+            }
+          }
+          store(c, hv[g], s0, s1, s2, s3);
+        }
+      }
+    } else {
+      for (int c = tid * 4; c < d; c += kGlueThreads * 4) {
+        const uint2 hv = *reinterpret_cast<const uint2*>(hr + c);
+        float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+        for (int r = 0; r < K; ++r) {
+          float4 o = o_row(r, 0, c);
+          for (int sl = 1; sl < splits; ++sl) {
+            const float4 u = o_row(r, sl, c);
+            o.x += u.x;
+            o.y += u.y;
+            o.z += u.z;
+            o.w += u.w;
+          }
+          const float wr = wt[r];
+          if (r == 0) {
+            s0 = wr * o.x, s1 = wr * o.y, s2 = wr * o.z, s3 = wr * o.w;
+          } else {
+            s0 = fmaf(wr, o.x, s0);
+            s1 = fmaf(wr, o.y, s1);
+            s2 = fmaf(wr, o.z, s2);
+            s3 = fmaf(wr, o.w, s3);
+          }
+        }
+        store(c, hv, s0, s1, s2, s3);
+      }
+    }
+  } else {
+    for (int c = tid * 4; c < d; c += kGlueThreads * 4)
+      *reinterpret_cast<uint2*>(xs + c) = *reinterpret_cast<const uint2*>(hr + c);
+  }
+  __syncthreads();
+  if (router) {
+    float sq = 0.0f;
+    for (int c = tid; c < d; c += 256) {
+      const float v = bf16_to_f32(xs[c]);
+      sq = fmaf(v, v, sq);
+    }
+    part[tid] = sq;
+  }
+  __syncthreads();
+  for (int m = 128; m >= 1; m >>= 1) {
+    if (tid < m) part[tid] += part[tid + m];
+    __syncthreads();
+  }
+  const float inv = 1.0f / sqrtf(part[0] / (float)d + eps);
+  bf16_t* xr = xn + t * d;
+  for (int c = tid * 4; c < d; c += kGlueThreads * 4) {
+    const uint2 hv = *reinterpret_cast<const uint2*>(xs + c);
+    uint2 xb;
+    xb.x = pack_bf16x2(__uint_as_float(hv.x << 16) * inv, __uint_as_float(hv.x & 0xffff0000u) * inv);
+    xb.y = pack_bf16x2(__uint_as_float(hv.y << 16) * inv, __uint_as_float(hv.y & 0xffff0000u) * inv);
+    *reinterpret_cast<uint2*>(xs + c) = xb;
+    *reinterpret_cast<uint2*>(xr + c) = xb;
+  }
+  __syncthreads();
+
+  // the router kernel's vector path with TPT = 256 (see vec_partials): the
+  // same chunks in the same order, the first kGluePrefetch from registers
+  for (int e0 = 0; router && e0 < E; e0 += 8) {
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+    int q = 0;
+    for (int k0 = tid * 8; k0 < d; k0 += 256 * 8, ++q) {
+      float xv[8];
+      bf16x8_to_f32(*reinterpret_cast<const uint4*>(xs + k0), xv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float wv[8];
+        if (e0 == 0 && q < kGluePrefetch) {
+          uint4 pre = wpre[0][i];
+#pragma unroll
+          for (int qq = 1; qq < kGluePrefetch; ++qq)
+            if (q == qq) pre = wpre[qq][i];
+          bf16x8_to_f32(pre, wv);
+        } else {
+          bf16x8_to_f32(*reinterpret_cast<const uint4*>(Wg + (int64_t)(k0 + i) * E + e0), wv);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(xv[i], wv[j], acc[j]);
+      }
+    }
+    const float sum = wave_sum8(acc, lane);             // value lane / 8
+    if ((lane & 7) == 0 && e0 + (lane >> 3) < E) wave_part[wave][e0 + (lane >> 3)] = sum;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float logit = 0.0f;
+  if (lane < E) {
+    for (int v = 0; v < 4; ++v) logit += wave_part[v][lane];
+  }
+  select_topk(logit, lane, E, K, topk_idx + t * K, topk_w + t * K);
+}
+
 template <typename T, int TPT, bool VEC>
 void launch_t(const void* x, const void* Wg, int T_, int d, int E, int K, int32_t* idx,
               float* w, float* logits, hipStream_t stream) {
@@ -278,6 +506,30 @@ void launch_t(const void* x, const void* Wg, int T_, int d, int E, int K, int32_
 }
 
 }  // namespace
+
+bool stack_glue_supported(int T, int d, int E, int dtype) {
+  return dtype == kBF16 && T < 1024 && E % 8 == 0 && d % 8 == 0 && d <= kStackGlueMaxD;
+}
+
+hipError_t launch_stack_glue(void* h, void* xn, const float* O, int o_splits, int64_t slice,
+                             float* topk_w, const int32_t* pos, int32_t* topk_idx, const void* Wg,
+                             int T, int d, int E, int K, float eps, hipStream_t stream) {
+  const int lds = d * (int)sizeof(bf16_t);
+  if (O) {
+    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(&stack_glue_kernel<true>), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(stack_glue_kernel<true>, dim3(T), dim3(kGlueThreads), lds, stream,
+                       static_cast<bf16_t*>(h), static_cast<bf16_t*>(xn), O, o_splits, slice,
+                       topk_w, pos, topk_idx, static_cast<const bf16_t*>(Wg), d, E, K, eps);
+  } else {
+    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(&stack_glue_kernel<false>), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(stack_glue_kernel<false>, dim3(T), dim3(kGlueThreads), lds, stream,
+                       static_cast<bf16_t*>(h), static_cast<bf16_t*>(xn), nullptr, 1, 0, topk_w,
+                       nullptr, topk_idx, static_cast<const bf16_t*>(Wg), d, E, K, eps);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_router_topk(const void* x, const void* Wg, int T, int d, int E, int K,
                               int dtype, int32_t* topk_idx, float* topk_w, float* logits,

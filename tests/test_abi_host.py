@@ -146,6 +146,31 @@ def test_noalloc_scratch_limit_and_noop(lib):
     assert _noalloc(lib, 0) == OK
 
 
+def test_stack_rejects_before_launch(lib):
+    E, L = 8, 2
+    ptrs = (ctypes.c_void_p * (L * E))(*([FAKE] * (L * E)))
+    wg = (ctypes.c_void_p * L)(FAKE, FAKE)
+    size = ctypes.c_size_t()
+    assert lib.moe_stack_workspace_size(8, 4096, 14336, E, 2, 1, ctypes.byref(size)) == OK
+    assert size.value >= M.workspace_size(8, 4096, 14336, E, 2, 1) + 8 * 4096 * 2
+
+    def call(h=FAKE2, wg=wg, w1=ptrs, L=L, T=8, d=4096, ws=FAKE, nbytes=None, eps=1e-5):
+        nbytes = size.value if nbytes is None else nbytes
+        return lib.moe_stack_forward(h, wg, w1, ptrs, ptrs, L, T, d, 14336, E, 2,
+                                     ctypes.c_float(eps), 1, None, ws, nbytes, None)
+
+    assert call(L=0) == OK and call(T=0) == OK
+    assert call(h=None) == EINVAL
+    assert call(wg=(ctypes.c_void_p * L)(FAKE, None)) == EINVAL
+    assert call(w1=(ctypes.c_void_p * (L * E))(*([FAKE] * (L * E - 1) + [None]))) == EINVAL
+    assert call(nbytes=size.value - 1) == EWORKSPACE
+    assert call(ws=FAKE + 16) == EWORKSPACE
+    assert call(ws=FAKE2) == EINVAL                      # workspace overlaps h
+    assert call(d=100) == EUNSUPPORTED
+    assert call(L=-1) == EINVAL
+    assert call(eps=-1.0) == EINVAL
+
+
 def test_stage_entry_points_validate(lib):
     arr = (ctypes.c_void_p * 8)(*([FAKE] * 8))
     assert lib.moe_router_topk(FAKE, FAKE, 4, 64, 8, 0, 1, FAKE, FAKE, None, None) == EINVAL

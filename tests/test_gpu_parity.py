@@ -489,10 +489,12 @@ def _stack_layerwise(blocks, stacks, K, tol, faithful, label):
     weights and outputs at the layer tolerances.
     The stack step (moe_stack_forward over that one block) must equal
     round(h_l + y_l) of that output bit for bit, and the whole stack run in
-    one call must equal the block-by-block result bit for bit.  Returns the
-    per-block errors of every stack."""
+    one call must equal the block-by-block result bit for bit, and the
+    per-block statistics it reports must hold each block's expert loads.
+    Returns the per-block errors of every stack."""
     hs = {name: h0.clone() for name, (h0, _) in stacks.items()}
     errs = {name: [] for name in stacks}
+    block_loads = {name: [] for name in stacks}
     for l, (Wg, W1, W3, W2) in enumerate(blocks):
         h_in, y_gpu, xn_gpu, gidx, gw, split = [], [], [], [], [], {}
         for name, (_, rows) in stacks.items():
@@ -508,6 +510,7 @@ def _stack_layerwise(blocks, stacks, K, tol, faithful, label):
             split[name] = (sum(len(a) for a in y_gpu), len(rows))
             y_gpu.append(PY.to_np(y32[sel]))
             xn_gpu.append(PY.to_np(xn[sel]))
+            block_loads[name].append(v["offsets"].diff().cpu().numpy().tolist())
             gidx.append(v["topk_idx"][sel].cpu().numpy())
             gw.append(v["topk_w"][sel].cpu().numpy())
             del v
@@ -530,9 +533,16 @@ def _stack_layerwise(blocks, stacks, K, tol, faithful, label):
         say("%s block %d: %s" % (label, l, ", ".join(line)))
     for name, (h0, _) in stacks.items():
         h = h0.clone()
-        M.moe_stack_forward(h, blocks, K)
+        E = len(blocks[0][1])
+        stats = torch.full((len(blocks), E + 1), -1, dtype=torch.int32, device=h.device)
+        M.moe_stack_forward(h, blocks, K, stats=stats)
         torch.cuda.synchronize()
         assert torch.equal(h, hs[name]), (label, name, "whole stack in one call")
+        st = stats.cpu().numpy()
+        T = h.shape[0]
+        assert np.all(st[:, :E].sum(axis=1) == T * K) and np.all(st[:, E] >= 0)
+        assert np.all(st[:, E] <= max(T - 1, 0))
+        assert st[:, :E].tolist() == block_loads[name]
     return errs
 
 
@@ -559,17 +569,16 @@ def test_stack_graph_replay_matches_eager(dev, T):
     w = small(name="stack32_bf16_T4096", T=T, d=256, d_ff=512, dtype="bf16")
     say("stack graph replay", T, M.plan_for(T, 256, 512, w.E, w.K, M.BF16))
     h0, blocks = _stack_inputs(w, dev, 3)
-    ws = torch.empty(M.workspace_size(w.T, w.d, w.d_ff, w.E, w.K, M.BF16), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(M.stack_workspace_size(w.T, w.d, w.d_ff, w.E, w.K, M.BF16),
+                     dtype=torch.uint8, device=dev)
     h = h0.clone()
-    xn = torch.empty_like(h)
-    M.moe_stack_forward(h, blocks, w.K, workspace=ws, xn=xn)
+    M.moe_stack_forward(h, blocks, w.K, workspace=ws)
     torch.cuda.synchronize()
     eager = h.clone()
     g = torch.cuda.CUDAGraph()
     h.copy_(h0)
     with torch.cuda.graph(g):
-        M.moe_stack_forward(h, blocks, w.K, workspace=ws, xn=xn)
+        M.moe_stack_forward(h, blocks, w.K, workspace=ws)
     for rep in range(4):
         h.copy_(h0)
         g.replay()
@@ -577,8 +586,32 @@ def test_stack_graph_replay_matches_eager(dev, T):
         assert torch.equal(h, eager), "replay %d" % rep
         # eager work between replays that reuses the same workspace
         h.copy_(h0)
-        M.moe_stack_forward(h, blocks[:1], w.K, workspace=ws, xn=xn)
+        M.moe_stack_forward(h, blocks[:1], w.K, workspace=ws)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("E,K,T,d,d_ff", [(6, 2, 8, 512, 256), (16, 4, 8, 512, 256),
+                                          (8, 2, 1, 512, 256), (8, 2, 2, 4096, 14336),
+                                          (8, 2, 4, 4096, 14336), (8, 2, 8, 4096, 14336)])
+def test_stack_glue_and_separate_launches_agree(dev, E, K, T, d, d_ff):
+    """The stack joins blocks with one glue launch when it can (8 | E) and
+    launches RMSNorm, router and combine separately otherwise; either way the
+    stack equals moe_rmsnorm + moe_forward(accumulate) block by block, bit
+    for bit.  The Mixtral-shape cases give the W2 product 4 and 2 slices (the
+    glue's all-loads-first combine); K = 4 and 7 slices (T = 1) take its
+    general loop."""
+    w = small(name="stack32_bf16_T4096", T=T, d=d, d_ff=d_ff, E=E, K=K)
+    say("stack glue", E, K, T, d, d_ff, M.plan_for(T, d, d_ff, E, K, M.BF16))
+    h0, blocks = _stack_inputs(w, dev, 3)
+    h = h0.clone()
+    for blk in blocks:
+        xn = M.moe_rmsnorm(h)
+        M.moe_forward(xn, *blk, K, y=h, accumulate=True)
+    ref = h.clone()
+    h = h0.clone()
+    M.moe_stack_forward(h, blocks, K)
+    torch.cuda.synchronize()
+    assert torch.equal(h, ref)
 
 
 @pytest.mark.timeout(900)
