@@ -36,6 +36,9 @@ SWEEP = ("mid_bf16_T512", "prefill_bf16_T4096_zipf")
 DECODE_SWEEP_T = (1, 2, 4, 16, 32, 64)
 STACK = "stack32_bf16_T4096"
 DECODE_STACK_T = 8
+SWEEP_MIN_STEPS = {"mid_bf16_T512": 50, "prefill_bf16_T4096_zipf": 20}
+CPU_SAMPLE_TOKENS = 64          # tokens of a sweep workload the oracle runs for its baseline
+STACK_STEPS = {4096: 5, 8: 20}  # timed steps of the 32-block stacks
 STAGES = ("router_topk", "route_permute", "expert_swiglu", "swiglu_finish", "expert_down",
           "combine")
 
@@ -82,7 +85,8 @@ class Layer:
         M.moe_expert_swiglu(self.x, self.W1, self.W3, w.K, self.offsets, self.sorted_token, self.H,
                             self.scratch, finish=False)
         mark(3)
-        M.moe_swiglu_finish(self.scratch, w.T, w.d, w.d_ff, w.E, w.K, M.BF16, self.H)
+        M.moe_swiglu_finish(self.scratch, w.T, w.d, w.d_ff, w.E, w.K, M.BF16, self.offsets,
+                            self.H)
         mark(4)
         M.moe_expert_down(self.H, self.W2, w.T, w.K, self.offsets, self.O)
         mark(5)
@@ -100,11 +104,13 @@ class Layer:
 
     def routing_stats(self):
         """Expert load and the share of consecutive tokens whose first-choice
-        expert repeats (uniform independent routing gives about 1/E)."""
-        idx = self.topk_idx.cpu().numpy()
-        first = idx[:, 0]
-        rep = float(np.mean(first[1:] == first[:-1])) if len(first) > 1 else None
-        return dict(first_choice_repeat_rate=None if rep is None else round(rep, 4))
+        expert repeats (uniform independent routing gives about 1/E), from
+        the routing-statistics kernel on the layer's routing table."""
+        counts, repeats = M.moe_routing_stats(self.topk_idx, self.w.E)
+        T = self.w.T
+        rep = int(repeats.item()) / (T - 1) if T > 1 else None
+        return dict(expert_counts=counts.cpu().numpy().tolist(),
+                    first_choice_repeat_rate=None if rep is None else round(rep, 4))
 
 
 def algorithmic(w: W.Workload, counts):
@@ -230,32 +236,65 @@ def measured_traffic(workload, plan):
     return None
 
 
+def traced_avg_ms(workload, plan):
+    """Average duration (ms) of the W1/W3 kernel in the committed rocprofv3
+    kernel-trace summary of this workload, or None when there is none or the
+    kernel's source changed since the trace was taken."""
+    kernel, src = swiglu_kernel(plan)
+    path = os.path.join(ROOT, "profiles", "%s_kernel_trace.txt" % workload)
+    try:
+        import hashlib
+        sha = hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest()
+        text = open(path).read()
+    except OSError:
+        return None
+    if ("%s: %s" % (src, sha)) not in text:
+        return None
+    for ln in text.splitlines():
+        r = [c.strip() for c in ln.split("|")]
+        if not ln.startswith("#") and len(r) >= 3 and r[0] == kernel:
+            return float(r[2]) / 1e3
+    return None
+
+
 def roofline_for(w, alg, per_stage_ms, plan):
+    """Roofline object of the W1/W3 kernel: `frac` from its HIP-event time in
+    this run, `frac_trace` from the average duration in the committed kernel
+    trace (null when that trace is of another source)."""
     g1_ms = per_stage_ms["expert_swiglu"]
     intensity = alg["swiglu_flops"] / alg["swiglu_bytes"]
     kernel = swiglu_kernel(plan)[0]
     traffic = measured_traffic(w.name, plan)
+    tr_ms = traced_avg_ms(w.name, plan)
     if intensity < 312:
-        achieved = alg["swiglu_bytes"] / (g1_ms * 1e-3) / 1e9
-        return dict(kernel=kernel, bound="hbm", achieved=round(achieved, 1),
-                    peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
-                    traffic=traffic, avg_ms=round(g1_ms, 4))
-    achieved = alg["swiglu_flops"] / (g1_ms * 1e-3) / 1e12
-    return dict(kernel=kernel, bound="mfma", achieved=round(achieved, 1),
-                peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=traffic,
-                avg_ms=round(g1_ms, 4))
+        work, scale, peak, bound, unit = alg["swiglu_bytes"], 1e9, HBM_PEAK_GBS, "hbm", "GB/s"
+    else:
+        work, scale, peak, bound, unit = (alg["swiglu_flops"], 1e12, MFMA_BF16_PEAK_TFLOPS,
+                                          "mfma", "TFLOP/s")
+    achieved = work / (g1_ms * 1e-3) / scale
+    out = dict(kernel=kernel, bound=bound, achieved=round(achieved, 1), peak=peak, unit=unit,
+               frac=round(achieved / peak, 4), traffic=traffic, avg_ms=round(g1_ms, 4),
+               trace_avg_ms=None if tr_ms is None else round(tr_ms, 4),
+               frac_trace=None if tr_ms is None else round(work / (tr_ms * 1e-3) / scale / peak,
+                                                           4))
+    return out
 
 
-def cpu_baseline(layer: Layer, max_tokens: int = 8):
-    """Float64 oracle on the first `max_tokens` tokens of the workload (all 8
-    for decode), weights copied to host outside the timed region."""
-    from oracle import moe_oracle as O
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(layer: Layer, max_tokens: int = 8, min_s: float = 10.0):
+    """Float64 oracle on the first `max_tokens` tokens of the workload (all 8
+    for decode), weights copied to host outside the timed region, repeated
+    until about `min_s` seconds of CPU work (at least 3 runs, or 1 when a run
+    takes longer than min_s)."""
+    from oracle import moe_oracle as O
+    threads = blas_threads()
     w = layer.w
     n = min(max_tokens, w.T)
     x = layer.x[:n].float().cpu().numpy()
@@ -264,12 +303,14 @@ def cpu_baseline(layer: Layer, max_tokens: int = 8):
     W3 = [t.float().cpu().numpy() for t in layer.W3]
     W2 = [t.float().cpu().numpy() for t in layer.W2]
     reps, t0 = 0, time.perf_counter()
-    while True:        # repeat the sample until ~10 s of CPU work (at least 3 runs)
+    while True:
         y_ref, aux = O.moe_forward(x, Wg, W1, W3, W2, w.K, faithful=True)
         reps += 1
-        if reps >= 3 and time.perf_counter() - t0 >= 10.0:
+        el = time.perf_counter() - t0
+        if el >= min_s and (reps >= 3 or el / reps >= min_s / 3):
             break
     dt = (time.perf_counter() - t0) / reps
+    del W1, W3, W2
     base = dict(value=round(n / dt, 3), unit="tokens/s", cores=int(threads), kind="oracle",
                 cpu_model=cpu_model(),
                 sample="first %d of %d tokens of %s, float64 oracle in faithful mode, "
@@ -347,7 +388,7 @@ def run_workload(name, dev, steps, warmup):
                ms_per_step_staged=round(wall_staged / steps * 1e3, 4),
                stage_ms={k: round(v, 4) for k, v in per_stage.items()},
                n_active_experts=alg["n_active"], expert_counts=counts.tolist(),
-               plan=layer.plan, routing=layer.routing_stats(),
+               plan=layer.plan, routing=layer.routing_stats(), warmup=warmup,
                layer_roofline_frac=round(max(alg["layer_bytes"] / (HBM_PEAK_GBS * 1e9),
                                              alg["layer_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12))
                                          / (ms * 1e-3), 4),
@@ -536,16 +577,40 @@ def run_dense_reference(dev, steps=10, warmup=3):
     return out
 
 
-def run_stacks(dev, steps, warmup, decode_steps):
+def stack_cpu_baseline(blocks, h0, K, n_tokens=16, n_blocks=2):
+    """The float64 oracle's pre-norm stack on a bounded sample: the first
+    n_tokens rows through the first n_blocks blocks (weights copied to host
+    outside the timed region).  Rows and blocks cost the same everywhere in
+    the stack, so the rate through all L blocks is n_tokens / (L x time per
+    block)."""
+    from oracle import moe_oracle as O
+    L = len(blocks)
+    h = h0[:n_tokens].float().cpu().numpy()
+    host = [(Wg.float().cpu().numpy(), [t.float().cpu().numpy() for t in W1],
+             [t.float().cpu().numpy() for t in W3], [t.float().cpu().numpy() for t in W2])
+            for Wg, W1, W3, W2 in blocks[:n_blocks]]
+    t0 = time.perf_counter()
+    O.stack_forward(h, host, K, faithful=True)
+    per_block = (time.perf_counter() - t0) / n_blocks
+    del host
+    return dict(value=round(n_tokens / (L * per_block), 4), unit="tokens/s (through all %d "
+                "blocks)" % L, cores=blas_threads(), kind="oracle", cpu_model=cpu_model(),
+                sample="first %d tokens through blocks 0-%d of %d, float64 oracle in faithful "
+                       "mode, %.2f s per block" % (n_tokens, n_blocks - 1, L, per_block))
+
+
+def run_stacks(dev, cpu=True):
     """The 32-block stack (RMSNorm + MoE + residual per block, 90 GB of
-    expert weights resident): T = 4096 tokens per step, and the same blocks
-    at T = 8 (decode through all 32 blocks, eager and replayed from a HIP
-    graph that holds the whole step)."""
+    expert weights resident), one moe_stack_forward call per step: T = 4096
+    tokens per step, and the same blocks at T = 8 (decode through all 32
+    blocks, eager and replayed from a HIP graph that holds the whole step)."""
     w = W.WORKLOADS[STACK]
     blocks = [W.expert_weights(w, dev, block=b) for b in range(w.layers)]
     weights_gb = w.layers * w.E * 3 * w.d * w.d_ff * 2 / 1e9
+    warmup = 1
     out = []
     for T in (w.T, DECODE_STACK_T):
+        decode_steps = steps = STACK_STEPS[T]
         h0 = W.make_x(w, blocks[0][0], dev, T=T)
         h = h0.clone()
         ws = torch.empty(M.stack_workspace_size(T, w.d, w.d_ff, w.E, w.K, M.BF16),
@@ -554,8 +619,8 @@ def run_stacks(dev, steps, warmup, decode_steps):
         def run():
             M.moe_stack_forward(h, blocks, w.K, workspace=ws)
 
-        t = _time_stack(h, h0, run, steps if T == w.T else decode_steps, warmup)
-        n = steps if T == w.T else decode_steps
+        t = _time_stack(h, h0, run, steps, warmup)
+        n = steps
         ms = t / n * 1e3
         res = dict(workload="stack32_bf16_T%d" % T, T=T, layers=w.layers, steps=n,
                    ms_per_step=round(ms, 3), tokens_per_s=round(T / (ms * 1e-3), 1),
@@ -593,6 +658,8 @@ def run_stacks(dev, steps, warmup, decode_steps):
             res["graph_tokens_per_s"] = round(T / (msg * 1e-3), 1)
             res["graph_hbm_frac"] = round(alg / (HBM_PEAK_GBS * 1e9) / (msg * 1e-3), 4)
             del g
+        if cpu and T == w.T:
+            res["cpu_baseline"] = stack_cpu_baseline(blocks, h0, w.K)
         out.append(res)
         del h, h0, ws
     del blocks
@@ -629,7 +696,7 @@ def main():
         print(json.dumps(dict(copy_bytes_read=n, copy_bytes_written=n, calls=args.steps)))
         return
     if args.only == "stack":
-        print(json.dumps(run_stacks(dev, 3, 1, 10)), flush=True)
+        print(json.dumps(run_stacks(dev, cpu=not args.no_cpu)), flush=True)
         return
     if args.only == "attention":
         print(json.dumps(run_attention(dev, args.steps, args.warmup, cpu=False)), flush=True)
@@ -648,19 +715,24 @@ def main():
     sweep = []
     if not args.no_sweep:
         for name in SWEEP:
-            r, lay = run_workload(name, dev, max(5, args.steps // 5), max(2, args.warmup // 2))
+            # at least 50 timed steps at T = 512 and 20 at T = 4096, 10 warm-up
+            r, lay = run_workload(name, dev, max(SWEEP_MIN_STEPS[name], args.steps),
+                                  max(10, args.warmup))
             print("# %s done: %.3f ms/step" % (name, r["ms_per_step"]), file=sys.stderr,
                   flush=True)
+            if not args.no_cpu:
+                r["cpu_baseline"], r["parity"] = cpu_baseline(lay, max_tokens=CPU_SAMPLE_TOKENS,
+                                                              min_s=6.0)
             sweep.append(r)
             del lay
             torch.cuda.empty_cache()
-    decode_sweep = [] if args.no_sweep else run_decode_sweep(dev, max(5, args.steps // 5), 2)
+    decode_sweep = [] if args.no_sweep else run_decode_sweep(dev, max(20, args.steps), 5)
     attention = [] if args.no_sweep else run_attention(dev, max(10, args.steps // 2), 3,
                                                        cpu=not args.no_cpu)
     for r in attention:
         print("# %s done: %.4f ms/call" % (r["workload"], r["ms_per_call"]), file=sys.stderr,
               flush=True)
-    stack = None if (args.no_sweep or args.no_stack) else run_stacks(dev, 3, 1, 10)
+    stack = None if (args.no_sweep or args.no_stack) else run_stacks(dev, cpu=not args.no_cpu)
     dense = None if args.no_sweep else run_dense_reference(dev)
     for r in dense or []:
         print("# dense %s (hipBLASLt) done: %.3f ms" % (r["product"], r["ms"]), file=sys.stderr,

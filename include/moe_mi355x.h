@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 #define MOE_MAX_EXPERTS 64
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -62,8 +62,10 @@ typedef enum {
  */
 typedef struct moe_plan {
   int32_t swiglu_splits;        /* W1/W3 product: 0 = fused (writes H itself); s >= 1 =  */
-                                /* fp32 partial sums over s K slices per matrix, which  */
-                                /* moe_swiglu_finish completes                          */
+                                /* fp32 partial sums over at most s K slices per matrix */
+                                /* (the kernels take the count for the number of token  */
+                                /* tiles that hold rows), which moe_swiglu_finish       */
+                                /* completes                                            */
   int32_t down_splits;          /* K splits of the W2 product = slices of O             */
   size_t swiglu_scratch_bytes;  /* fp32 partial sums the W1/W3 product needs (0 if none) */
   int32_t streaming;            /* 1: weight-streaming (small batch) kernels, 0: tiled   */
@@ -219,11 +221,14 @@ moe_status moe_expert_swiglu(const void* x, const void* const* W1, const void* c
 /*
  * Completes step 6 when plan.swiglu_splits > 0 (small batches): the fp32
  * partial sums that moe_expert_swiglu left in `scratch` are added in split
- * order and H = round(SiLU(a) * b) is written.  With plan.swiglu_splits == 0
- * H is already complete and this call does nothing (MOE_OK).
+ * order and H = round(SiLU(a) * b) is written.  offsets: the same expert
+ * offsets moe_expert_swiglu read (they fix how many K slices it wrote).
+ * With plan.swiglu_splits == 0 H is already complete and this call does
+ * nothing (MOE_OK).
  */
 moe_status moe_swiglu_finish(const void* scratch, int64_t T, int64_t d, int64_t d_ff, int32_t E,
-                             int32_t K, int32_t dtype, void* H, void* stream);
+                             int32_t K, int32_t dtype, const int32_t* offsets, void* H,
+                             void* stream);
 
 /*
  * Step 7 (code block D, second line): O_s[r] = H[r, k-slice s] W2[e][k-slice s]

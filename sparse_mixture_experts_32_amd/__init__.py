@@ -103,7 +103,7 @@ def load_library(path: str | None = None):
         "moe_expert_swiglu": (_c_i32, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32,
                                        _c_i32, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
         "moe_swiglu_finish": (_c_i32, [_c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_p,
-                                       _c_p]),
+                                       _c_p, _c_p]),
         "moe_expert_down": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
                                      _c_p, _c_p, _c_p]),
         "moe_combine": (_c_i32, [_c_p, _c_i32, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_i32,
@@ -321,13 +321,13 @@ def moe_expert_swiglu(x, W1, W3, K, offsets, sorted_token, H=None, scratch=None,
                                  scratch.numel() if scratch is not None else 0,
                                  _stream(stream)), lib)
     if finish and T:
-        moe_swiglu_finish(scratch, T, d, d_ff, E, K, dt, H, stream)
+        moe_swiglu_finish(scratch, T, d, d_ff, E, K, dt, offsets, H, stream)
     return H
 
 
-def moe_swiglu_finish(scratch, T, d, d_ff, E, K, dtype, H, stream=None):
+def moe_swiglu_finish(scratch, T, d, d_ff, E, K, dtype, offsets, H, stream=None):
     lib = load_library()
-    _check(lib.moe_swiglu_finish(_ptr(scratch), T, d, d_ff, E, K, dtype, _ptr(H),
+    _check(lib.moe_swiglu_finish(_ptr(scratch), T, d, d_ff, E, K, dtype, _ptr(offsets), _ptr(H),
                                  _stream(stream)), lib)
     return H
 

@@ -45,6 +45,8 @@
 //     per batch size by how the workgroups fill the chip (pick_launch), and
 //     a per-matrix W1/W3 split writes half the partial bytes of a split
 //     fused one for the same grid.
+#include <cmath>
+
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -53,6 +55,9 @@ namespace moe {
 namespace {
 
 struct StreamArgs {
+  // per-matrix W1/W3 launch: K split for each count of busy token tiles
+  // (index = busy tiles, up to kSplitTable - 1); `splits` is their maximum
+  int8_t split_of[kSplitTable];
   const bf16_t* A;         // [rows, Kdim] activations
   const int32_t* gather;   // sorted_token for gathered rows, else null
   const int32_t* offsets;  // [E + 1]
@@ -145,8 +150,19 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(StreamArgs a) {
   if (MODE == kPerMatrix) bid >>= 1;
   const int ftile = bid % tiles_f;
   bid /= tiles_f;
-  const int s = bid % a.splits;
-  const int ttile = bid / a.splits;
+  int s, ttile, splits = a.splits;
+  if (MODE == kPerMatrix) {
+    // split outermost: the per-matrix launch splits K by the number of token
+    // tiles that hold rows, known only here, and the workgroups of the
+    // unused splits come last and exit
+    ttile = bid % a.max_tiles;
+    s = bid / a.max_tiles;
+    splits = a.split_of[busy_tiles(a.offsets, a.E, 16 * NJ)];
+    if (s >= splits) return;
+  } else {
+    s = bid % a.splits;
+    ttile = bid / a.splits;
+  }
   int e, row_begin, row_end;
   if (!find_tile(a.offsets, a.E, 16 * NJ, ttile, e, row_begin, row_end)) return;
   e = __builtin_amdgcn_readfirstlane(e);
@@ -158,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(StreamArgs a) {
   const int mat = MODE == kPerMatrix ? mat_wg : wave / C::kKParts;
   const int kpart = wave % C::kKParts;
   const int f0 = ftile * kFeat;
-  const int kc = a.Kdim / a.splits;
+  const int kc = a.Kdim / splits;
   const int kw = kc / C::kKParts;
   const int kbeg = s * kc + kpart * kw;
   const int nsteps = kw / 32;
@@ -318,10 +334,14 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(StreamArgs a) {
 }
 
 // H[r][f] = bf16(SiLU(sum_s part[s][0][r][f]) * sum_s part[s][1][r][f]), slices
-// summed in order.
+// summed in order; the slice count is the one the W1/W3 launch took for the
+// number of busy token tiles.
 __global__ __launch_bounds__(256) void swiglu_finish_kernel(const float* __restrict__ part,
-                                                            int splits, int P, int N,
+                                                            SplitTable tab,
+                                                            const int32_t* __restrict__ offsets,
+                                                            int E, int P, int N,
                                                             bf16_t* __restrict__ H) {
+  const int splits = tab.split_of[busy_tiles(offsets, E, 16)];
   const int64_t n4 = (int64_t)P * N / 4;
   const int64_t slice = (int64_t)P * N;
   for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < n4;
@@ -388,6 +408,32 @@ int pick_launch(const double* wgs, int n) {
 
 }  // namespace
 
+// K split of the per-matrix W1/W3 launch when `tiles` token tiles hold rows
+// (0 if the shape cannot stream per matrix).  With one workgroup per compute
+// unit every round of workgroups takes as long as its slowest one, even a
+// round that is nearly empty (a lone workgroup streams at one compute unit's
+// rate), and every workgroup pays a fixed cost besides its share of K.
+// Measured at Mixtral shape, T = 8, busy tiles 2..8 and splits 1, 2, 4, the
+// time follows rounds x (1/s + 0.11); the split minimising that is taken,
+// the smaller one on ties.
+constexpr double kSplitFixedCost = 0.11;
+
+int per_matrix_split(int d, int d_ff, double tiles) {
+  const double per = tiles * (d_ff / kFeat);
+  int best = 0;
+  double best_cost = 0.0;
+  for (int s = 1; s <= 64; ++s) {
+    if (!stream_shape_ok(d, d_ff, kWaves, s)) continue;
+    const double rounds = std::ceil(2.0 * s * per / kComputeUnits - 1e-9);
+    const double cost = std::max(rounds, 1.0) * (1.0 / s + kSplitFixedCost);
+    if (best == 0 || cost < best_cost - 1e-12) {
+      best = s;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 int stream_swiglu_splits(int d, int d_ff, double tiles) {
   if (!stream_shape_ok(d, d_ff, kWaves / 2, 1)) return -1;
   const double per = tiles * (d_ff / kFeat);  // busy workgroups of the fused launch
@@ -401,7 +447,20 @@ int stream_swiglu_splits(int d, int d_ff, double tiles) {
       wgs[n] = 2.0 * s * per;
       split[n++] = s;
     }
-  return split[pick_launch(wgs, n)];
+  const int pick = split[pick_launch(wgs, n)];
+  if (pick == 0) return 0;
+  // per matrix: room for the largest split any busy-tile count may take
+  int most = pick;
+  for (int b = 1; b < kSplitTable; ++b) most = std::max(most, per_matrix_split(d, d_ff, b));
+  return most;
+}
+
+SplitTable stream_split_table(int d, int d_ff, int P, int E) {
+  SplitTable t{};
+  const int max_tiles = std::min((P + E * 15) / 16, kSplitTable - 1);
+  for (int b = 0; b < kSplitTable; ++b)
+    t.split_of[b] = (int8_t)std::max(1, per_matrix_split(d, d_ff, std::min(b, max_tiles)));
+  return t;
 }
 
 int stream_down_splits(int d_ff, int d, double tiles) {
@@ -439,16 +498,19 @@ hipError_t launch_stream_swiglu_bf16(const void* x, const int32_t* sorted_token,
     a.splits = 1;
     return launch_stream<1, kFused>(a, stream);
   }
+  const SplitTable tab = stream_split_table(d, d_ff, P, E);
+  for (int b = 0; b < kSplitTable; ++b) a.split_of[b] = tab.split_of[b];
   return launch_stream<1, kPerMatrix>(a, stream);
 }
 
-hipError_t launch_swiglu_finish_bf16(const float* part, int splits, int P, int d_ff, void* H,
-                                     hipStream_t stream) {
+hipError_t launch_swiglu_finish_bf16(const float* part, const int32_t* offsets, int P, int d,
+                                     int d_ff, int E, void* H, hipStream_t stream) {
   const int64_t n4 = (int64_t)P * d_ff / 4;
   if (n4 == 0) return hipSuccess;
   const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 2048);
-  hipLaunchKernelGGL(swiglu_finish_kernel, dim3(blocks), dim3(256), 0, stream, part, splits, P,
-                     d_ff, static_cast<bf16_t*>(H));
+  hipLaunchKernelGGL(swiglu_finish_kernel, dim3(blocks), dim3(256), 0, stream, part,
+                     stream_split_table(d, d_ff, P, E), offsets, E, P, d_ff,
+                     static_cast<bf16_t*>(H));
   return hipGetLastError();
 }
 

@@ -333,8 +333,8 @@ moe_status run_experts(const Plan& plan, const void* x, const moe::ExpertPtrs& p
                  b.scratch, st);
   if (e != hipSuccess) return hip_status(e, "expert_swiglu");
   if (plan.swiglu_splits > 0) {
-    e = moe::launch_swiglu_finish_bf16(static_cast<const float*>(b.scratch), plan.swiglu_splits,
-                                       P, (int)d_ff, b.H, st);
+    e = moe::launch_swiglu_finish_bf16(static_cast<const float*>(b.scratch), b.offsets, P,
+                                       (int)d, (int)d_ff, E, b.H, st);
     if (e != hipSuccess) return hip_status(e, "swiglu_finish");
   }
   e = run_down(plan, b.H, p2, b.offsets, P, (int)d, (int)d_ff, E, dtype, b.O, st);
@@ -373,16 +373,17 @@ moe_status moe_expert_swiglu(const void* x, const void* const* W1, const void* c
 }
 
 moe_status moe_swiglu_finish(const void* scratch, int64_t T, int64_t d, int64_t d_ff, int32_t E,
-                             int32_t K, int32_t dtype, void* H, void* stream) {
+                             int32_t K, int32_t dtype, const int32_t* offsets, void* H,
+                             void* stream) {
   moe_status s = check_shape(T, d, d_ff, E, K, dtype);
   if (s) return s;
   const Plan plan = make_plan(T, d, d_ff, E, K, dtype);
   if (T == 0 || plan.swiglu_splits == 0) return ok();
-  if (!scratch || !H) return fail(MOE_EINVAL, "NULL pointer");
+  if (!scratch || !H || !offsets) return fail(MOE_EINVAL, "NULL pointer");
   if (!aligned16(scratch) || !aligned16(H))
     return fail(MOE_EUNSUPPORTED, "scratch and H must be 16-byte aligned");
-  return finish(moe::launch_swiglu_finish_bf16(static_cast<const float*>(scratch),
-                                               plan.swiglu_splits, (int)(T * K), (int)d_ff, H,
+  return finish(moe::launch_swiglu_finish_bf16(static_cast<const float*>(scratch), offsets,
+                                               (int)(T * K), (int)d, (int)d_ff, E, H,
                                                (hipStream_t)stream),
                 "swiglu_finish");
 }

@@ -55,10 +55,13 @@ hipError_t launch_expert_down_f32(const void* H, const ExpertPtrs& W2, const int
 // most 16 rows per token tile), N in tiles of kStreamFeat features.
 constexpr int kStreamFeat = 256;
 // W1/W3 launch when about `tiles` token tiles hold rows: 0 = fused (H written
-// by the product), s >= 1 = one matrix per workgroup with K split s ways
-// (fp32 partial sums, completed by launch_swiglu_finish_bf16); -1 if the
-// shape cannot stream.
+// by the product), s >= 1 = one matrix per workgroup with K split up to s
+// ways (fp32 partial sums, completed by launch_swiglu_finish_bf16); -1 if the
+// shape cannot stream.  The per-matrix launch takes its split count from
+// stream_split_table by the number of token tiles that hold rows, which the
+// kernels count from the expert offsets.
 int stream_swiglu_splits(int d, int d_ff, double tiles);
+SplitTable stream_split_table(int d, int d_ff, int P, int E);
 // W2 K split (slices of O) for about `tiles` busy token tiles; 0 if the
 // shape cannot stream.
 int stream_down_splits(int d_ff, int d, double tiles);
@@ -66,9 +69,10 @@ hipError_t launch_stream_swiglu_bf16(const void* x, const int32_t* sorted_token,
                                      const ExpertPtrs& W1, const ExpertPtrs& W3,
                                      const int32_t* offsets, int P, int d, int d_ff, int E,
                                      int splits, float* part, void* H, hipStream_t stream);
-// H[r][f] = bf16(SiLU(sum_s part[s][0][r][f]) * sum_s part[s][1][r][f]).
-hipError_t launch_swiglu_finish_bf16(const float* part, int splits, int P, int d_ff, void* H,
-                                     hipStream_t stream);
+// H[r][f] = bf16(SiLU(sum_s part[s][0][r][f]) * sum_s part[s][1][r][f]), over
+// the splits the W1/W3 launch took.
+hipError_t launch_swiglu_finish_bf16(const float* part, const int32_t* offsets, int P, int d,
+                                     int d_ff, int E, void* H, hipStream_t stream);
 hipError_t launch_stream_down_bf16(const void* H, const ExpertPtrs& W2, const int32_t* offsets,
                                    int P, int d, int d_ff, int E, int splits, float* O,
                                    hipStream_t stream);

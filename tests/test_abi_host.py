@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
     assert lib.moe_status_str(0) == b"MOE_OK"
     assert lib.moe_status_str(4) == b"MOE_EHIP"
 
