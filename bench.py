@@ -210,11 +210,12 @@ CSRC = os.path.join(ROOT, "sparse_mixture_experts_32_amd", "csrc")
 
 def swiglu_kernel(plan):
     """(kernel name as the profiler prints it, source file) of the W1/W3
-    stage: the streaming kernel in its fused (1) or per-matrix (2) form, or
-    the tiled kernel."""
+    stage: the streaming kernel in its fused form, the per-matrix streaming
+    kernel over a persistent grid, or the tiled kernel."""
     if plan["streaming"]:
-        form = 1 if plan["swiglu_splits"] == 0 else 2
-        return "stream_gemm_kernel<1, %d>" % form, "expert_stream_bf16.hip"
+        if plan["swiglu_splits"] == 0:
+            return "stream_gemm_kernel<1, 1>", "expert_stream_bf16.hip"
+        return "stream_sk_kernel", "expert_stream_bf16.hip"
     return "tiled_gemm_kernel<256, true>", "expert_tiled_bf16.hip"
 
 

@@ -30,21 +30,20 @@
 //   * a workgroup has eight waves (two per SIMD, one workgroup per compute
 //     unit) and every wave streams one matrix.  The W2 product puts all
 //     eight on W2, splitting the workgroup's k-range eight ways.  The W1/W3
-//     product runs one of two ways (StreamMode): fused -- waves 0-3 on W1,
-//     4-7 on W3, each four splitting the whole of K, and H = bf16(SiLU(a) *
-//     b) stored by the epilogue -- or per matrix -- W1 and W3 in alternate
-//     workgroups, K split over `splits` workgroups, fp32 partial sums of a
-//     and b stored for swiglu_finish_kernel (its own launch), which adds the
-//     slices in order and applies SwiGLU.  The waves' partial products meet
-//     in LDS and are added in wave order;
+//     product runs one of two ways: fused (stream_gemm_kernel) -- waves 0-3
+//     on W1, 4-7 on W3, each four splitting the whole of K, and H =
+//     bf16(SiLU(a) * b) stored by the epilogue -- or per matrix
+//     (stream_sk_kernel) -- one matrix at a time over a persistent grid that
+//     gives every compute unit the same number of weight rows, fp32 partial
+//     sums of a and b stored for swiglu_finish_kernel (its own launch), which
+//     adds the slices in order and applies SwiGLU.  The waves' partial
+//     products meet in LDS and are added in wave order;
 //   * K splits write fp32 partial sums to separate slices (non-temporal
 //     stores), summed later in slice order, so results are deterministic.
 //     Every partial byte written costs streaming time -- a loads-only
 //     replica slowed by 13 % when its workgroups also wrote 1.6 % as many
 //     bytes as they read -- so the launch form and split count are chosen
-//     per batch size by how the workgroups fill the chip (pick_launch), and
-//     a per-matrix W1/W3 split writes half the partial bytes of a split
-//     fused one for the same grid.
+//     per batch size by how the workgroups fill the chip (pick_launch).
 #include <cmath>
 
 #include "moe_common.h"
@@ -55,9 +54,6 @@ namespace moe {
 namespace {
 
 struct StreamArgs {
-  // per-matrix W1/W3 launch: K split for each count of busy token tiles
-  // (index = busy tiles, up to kSplitTable - 1); `splits` is their maximum
-  int8_t split_of[kSplitTable];
   const bf16_t* A;         // [rows, Kdim] activations
   const int32_t* gather;   // sorted_token for gathered rows, else null
   const int32_t* offsets;  // [E + 1]
@@ -114,8 +110,9 @@ constexpr int kFeat = kStreamFeat;  // features per workgroup (and per wave)
 // units beats more, shorter workgroups; without one, an unsplit product of
 // at least 1.7 rounds (no partial sums, no finish launch) beats splitting,
 // and otherwise about three rounds do best.  For Mixtral's shapes at 1, 2,
-// 4, 8, 16, 32 tokens this gives W1/W3 per matrix with 1, fused, 2, 1 splits,
-// then fused; W2 with 7, 4, 2, 2, 2, 2 splits.
+// 4, 8, 16, 32 tokens this gives W1/W3 per matrix, fused, per matrix, per
+// matrix, fused, fused (the per-matrix form then runs over its persistent
+// grid); W2 with 7, 4, 2, 2, 2, 2 splits.
 constexpr double kComputeUnits = 256;
 constexpr int kLoads = 16;          // 16-byte loads per lane per k-step of 32
 
@@ -123,12 +120,8 @@ constexpr int kLoads = 16;          // 16-byte loads per lane per k-step of 32
 //   kDown:      one matrix (W2); partial sums to O slices.
 //   kFused:     W1 and W3 in every workgroup (waves 0-3 / 4-7), no K split;
 //               H = bf16(SiLU(a) * b) in the epilogue.
-//   kPerMatrix: W1 and W3 in alternate workgroups, all eight waves on one
-//               matrix, K split `splits` ways; fp32 partial sums of a and b
-//               to scratch slices [split][matrix], summed by
-//               swiglu_finish_kernel.  Half the partial-sum bytes of
-//               splitting a fused workgroup's K range for the same grid.
-enum StreamMode { kDown = 0, kFused = 1, kPerMatrix = 2 };
+// (The per-matrix W1/W3 form is stream_sk_kernel below.)
+enum StreamMode { kDown = 0, kFused = 1 };
 
 template <int NJ, int MODE>
 struct StreamCfg {
@@ -136,6 +129,41 @@ struct StreamCfg {
   static constexpr int kMatsWG = MODE == kFused ? 2 : 1;  // matrices inside a workgroup
   static constexpr int kKParts = kWaves / kMatsWG;        // waves sharing one matrix
 };
+
+// One k-step of 32 rows: the 16 loaded weight registers w are transposed
+// into MFMA operands and multiplied with the token operand b.
+//   t: k-rows 0-7 (lanes 0-31) / 8-15 (lanes 32-63); u: 16-23 / 24-31.
+//   Lanes 0-15 and 32-47 hold features 0-127, lanes 16-31 and 48-63
+//   features 128-255.
+template <int NJ>
+__device__ __forceinline__ void mma_step(const u32x4_t (&w)[kLoads], const u32x4_t (&b)[NJ],
+                                         f32x4_t (&acc)[2][8][NJ]) {
+  bf16x8_t bo[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) bo[j] = __builtin_bit_cast(bf16x8_t, b[j]);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const u32x4_t t = column(w, c);
+    const u32x4_t u = column(w + 8, c);
+    u32x4_t lo, hi;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const auto r = __builtin_amdgcn_permlane16_swap(t[v], u[v], false, false);
+      lo[v] = r[0];  // rows t0, u0, t2, u2: features 0-127, k-groups 0, 16, 8, 24
+      hi[v] = r[1];  // rows t1, u1, t3, u3: features 128-255, same k-groups
+    }
+    const bf16x8_t opl = __builtin_bit_cast(bf16x8_t, lo);
+    const bf16x8_t oph = __builtin_bit_cast(bf16x8_t, hi);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      acc[0][c][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(opl, bo[j], acc[0][c][j], 0, 0, 0);
+      acc[1][c][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oph, bo[j], acc[1][c][j], 0, 0, 0);
+    }
+    // one column at a time: forming all eight operands first would hold
+    // 64 more registers
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
 
 template <int NJ, int MODE>
 __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(StreamArgs a) {
@@ -146,23 +174,11 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(StreamArgs a) {
 
   const int tiles_f = a.N / kFeat;
   int bid = blockIdx.x;
-  const int mat_wg = MODE == kPerMatrix ? (bid & 1) : 0;
-  if (MODE == kPerMatrix) bid >>= 1;
   const int ftile = bid % tiles_f;
   bid /= tiles_f;
-  int s, ttile, splits = a.splits;
-  if (MODE == kPerMatrix) {
-    // split outermost: the per-matrix launch splits K by the number of token
-    // tiles that hold rows, known only here, and the workgroups of the
-    // unused splits come last and exit
-    ttile = bid % a.max_tiles;
-    s = bid / a.max_tiles;
-    splits = a.split_of[busy_tiles(a.offsets, a.E, 16 * NJ)];
-    if (s >= splits) return;
-  } else {
-    s = bid % a.splits;
-    ttile = bid / a.splits;
-  }
+  const int s = bid % a.splits;
+  const int ttile = bid / a.splits;
+  const int splits = a.splits;
   int e, row_begin, row_end;
   if (!find_tile(a.offsets, a.E, 16 * NJ, ttile, e, row_begin, row_end)) return;
   e = __builtin_amdgcn_readfirstlane(e);
@@ -171,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(StreamArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int mat = MODE == kPerMatrix ? mat_wg : wave / C::kKParts;
+  const int mat = wave / C::kKParts;
   const int kpart = wave % C::kKParts;
   const int f0 = ftile * kFeat;
   const int kc = a.Kdim / splits;
@@ -233,34 +249,7 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(StreamArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   };
   auto compute = [&](const u32x4_t (&w)[kLoads], const u32x4_t (&b)[NJ]) {
-    bf16x8_t bo[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) bo[j] = __builtin_bit_cast(bf16x8_t, b[j]);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      // t: k-rows 0-7 (lanes 0-31) / 8-15 (lanes 32-63); u: 16-23 / 24-31.
-      // Lanes 0-15 and 32-47 hold features 0-127, lanes 16-31 and 48-63
-      // features 128-255.
-      const u32x4_t t = column(w, c);
-      const u32x4_t u = column(w + 8, c);
-      u32x4_t lo, hi;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const auto r = __builtin_amdgcn_permlane16_swap(t[v], u[v], false, false);
-        lo[v] = r[0];  // rows t0, u0, t2, u2: features 0-127, k-groups 0, 16, 8, 24
-        hi[v] = r[1];  // rows t1, u1, t3, u3: features 128-255, same k-groups
-      }
-      const bf16x8_t opl = __builtin_bit_cast(bf16x8_t, lo);
-      const bf16x8_t oph = __builtin_bit_cast(bf16x8_t, hi);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        acc[0][c][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(opl, bo[j], acc[0][c][j], 0, 0, 0);
-        acc[1][c][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oph, bo[j], acc[1][c][j], 0, 0, 0);
-      }
-      // one column at a time: forming all eight operands first would hold
-      // 64 more registers
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    mma_step<NJ>(w, b, acc);
   };
 
   // The first weight loads need only the expert; the token rows wait for
@@ -323,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(StreamArgs a) {
       } else {
 #pragma unroll
         for (int m = 0; m < MW; ++m) {
-          const int slice = s * C::kSlices + (MODE == kPerMatrix ? mat_wg : m);
+          const int slice = s * C::kSlices + m;
           f32x4_t* dst = reinterpret_cast<f32x4_t*>(a.part + ((int64_t)slice * a.P + r) * N + f);
           __builtin_nontemporal_store(f32x4_t{sum[m][0], sum[m][1], sum[m][2], sum[m][3]}, dst);
           __builtin_nontemporal_store(f32x4_t{sum[m][4], sum[m][5], sum[m][6], sum[m][7]}, dst + 1);
@@ -333,25 +322,242 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(StreamArgs a) {
   }
 }
 
-// H[r][f] = bf16(SiLU(sum_s part[s][0][r][f]) * sum_s part[s][1][r][f]), slices
-// summed in order; the slice count is the one the W1/W3 launch took for the
-// number of busy token tiles.
+// ---- per-matrix W1/W3 product over a persistent grid (stream-K) ----
+//
+// Work units are (busy token tile, feature tile of 256, matrix), numbered
+// u = (tile * tiles_f + ftile) * 2 + matrix, each K = Kdim rows long and cut
+// into chunks of kChunkRows rows (two k-steps per wave).  With G workgroups
+// (one per compute unit):
+//   * U >= G units: workgroup w takes chunks [w C / G, (w+1) C / G) of the
+//     C = U * (Kdim / kChunkRows) chunks in unit order, so every workgroup
+//     streams the same number of weight bytes and no round of workgroups is
+//     left nearly empty.  A unit is cut at most once; its head piece goes
+//     to partial-sum slice 0, its tail to slice 1.
+//   * U < G: every unit is cut into the same number s of pieces (the largest
+//     power of two with U s <= G dividing the chunk count), piece i to
+//     slice i.
+// Inside a piece the eight waves split its rows evenly, as in the per-matrix
+// launch (a whole-unit piece sums exactly as that launch's unsplit product).
+// The weight and token loads of the next piece's first k-step are issued
+// before the current piece's epilogue, and the epilogue synchronises the
+// waves through LDS only, so those loads stay in flight across it.
+constexpr int kChunkRows = 2 * 32 * kWaves;
+constexpr int kStreamMaxPairs = 64;   // the streaming plan takes T * K <= 64
+
+__device__ __forceinline__ int sk_small_split(int U, int G, int cpu) {
+  int s = 1;
+  while (cpu % (2 * s) == 0 && (int64_t)U * 2 * s <= G) s *= 2;
+  return s;
+}
+
+// Whether unit u of the stream-K layout (U >= G) is cut by a workgroup
+// boundary: the boundaries are floor(w C / G); the owner of the unit's first
+// chunk is the largest w with floor(w C / G) <= u cpu.
+__device__ __forceinline__ bool sk_unit_split(int64_t u, int64_t C, int G, int cpu) {
+  const int64_t c = u * cpu;
+  const int64_t w0 = ((c + 1) * G + C - 1) / C - 1;
+  return w0 + 1 < G && ((w0 + 1) * C) / G < c + cpu;
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__global__ __launch_bounds__(kThreads) void stream_sk_kernel(StreamArgs a) {
+  constexpr int NJ = 1;
+  __shared__ f32x4_t red[kWaves * 8 * NJ * 64];
+  // the routing tables of the batch (at most 64 pairs), read once: later
+  // reads come from LDS, not from memory the kernel also writes
+  __shared__ int32_t sh_off[kMaxExperts + 1];
+  __shared__ int32_t sh_tok[kStreamMaxPairs];
+  if ((int)threadIdx.x <= a.E) sh_off[threadIdx.x] = a.offsets[threadIdx.x];
+  if ((int)threadIdx.x < a.P) sh_tok[threadIdx.x] = a.gather[threadIdx.x];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tiles_f = a.N / kFeat;
+  const int G = gridDim.x;
+  const int w = blockIdx.x;
+  const int cpu = a.Kdim / kChunkRows;
+  const int U = busy_tiles(sh_off, a.E, 16) * tiles_f * 2;
+  int64_t c_beg, c_end;
+  int small_slice = -1;
+  if (U >= G) {
+    const int64_t C = (int64_t)U * cpu;
+    c_beg = (int64_t)w * C / G;
+    c_end = (int64_t)(w + 1) * C / G;
+  } else {
+    const int s = sk_small_split(U, G, cpu);
+    if (w >= U * s) return;
+    const int per = cpu / s;
+    small_slice = w % s;
+    c_beg = (int64_t)(w / s) * cpu + small_slice * per;
+    c_end = c_beg + per;
+  }
+  const int64_t N = a.N;
+  const int64_t row_bytes = N * 2;
+  const int lane_off = (lane >> 5) * 8 * (int)row_bytes + (lane & 31) * 16;
+  const int kofs = 8 * ((lane >> 4) >> 1) + 16 * ((lane >> 4) & 1);
+
+  struct Piece {
+    const char* wbase;      // this wave's first weight row of the piece
+    const bf16_t* bsrc;     // this lane's token row at the wave's first k
+    int nsteps;             // k-steps of 32 rows per wave (0: no piece)
+    int row_begin, row_end, f0, mat, slice;
+    int64_t next;           // first chunk after the piece
+  };
+  auto make_piece = [&](int64_t c) {
+    Piece p;
+    const int64_t u = c / cpu;
+    const int pc0 = (int)(c - u * cpu);
+    const int pc1 = (int)min((int64_t)cpu, c_end - u * cpu);
+    p.mat = (int)(u & 1);
+    const int ftile = (int)((u >> 1) % tiles_f);
+    const int bt = (int)((u >> 1) / tiles_f);
+    int e = 0, rb = 0, re = 1;
+    find_tile(sh_off, a.E, 16, bt, e, rb, re);
+    p.row_begin = __builtin_amdgcn_readfirstlane(rb);
+    p.row_end = __builtin_amdgcn_readfirstlane(re);
+    e = __builtin_amdgcn_readfirstlane(e);
+    p.f0 = ftile * kFeat;
+    p.slice = small_slice >= 0 ? small_slice : (pc0 == 0 ? 0 : 1);
+    const int kw = (pc1 - pc0) * (kChunkRows / kWaves);
+    const int kbeg = pc0 * kChunkRows + wave * kw;
+    p.nsteps = kw / 32;
+    p.wbase = reinterpret_cast<const char*>(p.mat == 0 ? a.Wa.p[e] : a.Wb.p[e]) +
+              ((int64_t)kbeg * N + p.f0) * 2;
+    const int r = min(p.row_begin + (lane & 15), p.row_end - 1);
+    p.bsrc = a.A + (int64_t)sh_tok[r] * a.Kdim + kbeg + kofs;
+    p.next = u * cpu + pc1;
+    return p;
+  };
+
+  f32x4_t acc[2][8][NJ];
+  u32x4_t w0[kLoads], w1[kLoads];
+  u32x4_t b0[NJ], b1[NJ];
+
+  // weight rows of k-step `step` of a piece: a zero-size resource when the
+  // piece is empty, so the loads return zeros without a memory access
+  auto load_w = [&](u32x4_t (&wr)[kLoads], const char* base, int step, bool live) {
+    const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(base) + (int64_t)step * 32 * row_bytes, (short)0,
+        live ? 32 * (int)row_bytes : 0, kBufferWord3);
+#pragma unroll
+    for (int r = 0; r < kLoads; ++r) {
+      const int row = (r & 7) + 16 * (r >> 3);
+      wr[r] = __builtin_amdgcn_raw_buffer_load_b128(res, lane_off, row * (int)row_bytes,
+                                                    kNonTemporal);
+    }
+  };
+  auto load_b = [&](u32x4_t (&b)[NJ], const bf16_t* src) {
+    b[0] = *reinterpret_cast<const u32x4_t*>(src);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  Piece cur = make_piece(c_beg);
+  load_w(w0, cur.wbase, 0, true);
+  __builtin_amdgcn_sched_barrier(0);
+  load_b(b0, cur.bsrc);
+  while (true) {
+    Piece nxt = cur;
+    nxt.nsteps = 0;
+    if (cur.next < c_end) nxt = make_piece(cur.next);
+    const bool more = nxt.nsteps > 0;
+    // past the last piece the token loads reread the current piece's last step
+    const bf16_t* b_after = more ? nxt.bsrc : cur.bsrc + (cur.nsteps - 1) * 32;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[h][c][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < cur.nsteps; i += 2) {
+      load_w(w1, cur.wbase, i + 1, true);
+      load_b(b1, cur.bsrc + (i + 1) * 32);
+      mma_step<NJ>(w0, b0, acc);
+      // k-step i + 2: this piece's, or the next piece's first
+      const bool inside = i + 2 < cur.nsteps;
+      load_w(w0, inside ? cur.wbase : nxt.wbase, inside ? i + 2 : 0, inside || more);
+      load_b(b0, inside ? cur.bsrc + (i + 2) * 32 : b_after);
+      mma_step<NJ>(w1, b1, acc);
+    }
+
+    // epilogue: the waves' partial products meet in LDS, added in wave
+    // order; one feature half at a time
+    const float* redf = reinterpret_cast<const float*>(red);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h) lds_barrier();  // the first half's reads are done
+#pragma unroll
+      for (int c = 0; c < 8; ++c) red[(wave * 8 + c) * 64 + lane] = acc[h][c][0];
+      lds_barrier();
+      for (int o = threadIdx.x; o < 256; o += kThreads) {
+        const int L = o & 63;
+        const int q = (o >> 6) & 3;
+        const int r = cur.row_begin + (L & 15);
+        if (r >= cur.row_end) continue;
+        const int f = cur.f0 + 128 * h + 8 * (4 * (L >> 4) + q);
+        float sum[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          float t = redf[((c * 64) + L) * 4 + q];
+#pragma unroll
+          for (int v = 1; v < kWaves; ++v) t += redf[(((v * 8 + c) * 64) + L) * 4 + q];
+          sum[c] = t;
+        }
+        const int slice = cur.slice * 2 + cur.mat;
+        f32x4_t* dst = reinterpret_cast<f32x4_t*>(a.part + ((int64_t)slice * a.P + r) * N + f);
+        __builtin_nontemporal_store(f32x4_t{sum[0], sum[1], sum[2], sum[3]}, dst);
+        __builtin_nontemporal_store(f32x4_t{sum[4], sum[5], sum[6], sum[7]}, dst + 1);
+      }
+    }
+    lds_barrier();  // before the next piece's epilogue writes the LDS again
+    if (!more) break;
+    cur = nxt;
+  }
+}
+
+// H[r][f] = bf16(SiLU(a) * b), a and b the sums of their matrix's partial
+// slices in slice order: the slices stream_sk_kernel wrote for the unit of
+// (r, f), i.e. one, or two for a unit cut by a workgroup boundary, or the s
+// equal pieces when there are fewer units than workgroups.  Rows past the
+// last expert segment belong to no unit and are left alone.
 __global__ __launch_bounds__(256) void swiglu_finish_kernel(const float* __restrict__ part,
-                                                            SplitTable tab,
                                                             const int32_t* __restrict__ offsets,
-                                                            int E, int P, int N,
+                                                            int E, int P, int N, int Kdim, int G,
                                                             bf16_t* __restrict__ H) {
-  const int splits = tab.split_of[busy_tiles(offsets, E, 16)];
+  const int tiles_f = N / kFeat;
+  const int U = busy_tiles(offsets, E, 16) * tiles_f * 2;
+  const int cpu = Kdim / kChunkRows;
+  const int s_small = U < G ? sk_small_split(U, G, cpu) : 0;
+  const int64_t C = (int64_t)U * cpu;
   const int64_t n4 = (int64_t)P * N / 4;
   const int64_t slice = (int64_t)P * N;
   for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < n4;
        g += (int64_t)gridDim.x * blockDim.x) {
+    const int r = (int)(g / (N / 4));
+    const int f = (int)(g % (N / 4)) * 4;
+    int bt = 0, e = 0;
+    for (; e < E; ++e) {
+      const int lo = offsets[e], hi = offsets[e + 1];
+      if (r < hi) {
+        bt += (r - lo) / 16;
+        break;
+      }
+      bt += (hi - lo + 15) / 16;
+    }
+    if (e == E) continue;
+    const int64_t u = ((int64_t)bt * tiles_f + f / kFeat) * 2;
+    const int na = s_small ? s_small : (sk_unit_split(u, C, G, cpu) ? 2 : 1);
+    const int nb = s_small ? s_small : (sk_unit_split(u + 1, C, G, cpu) ? 2 : 1);
     float4 av = reinterpret_cast<const float4*>(part)[g];
     float4 bv = reinterpret_cast<const float4*>(part + slice)[g];
-    for (int s = 1; s < splits; ++s) {
-      const float4 x = reinterpret_cast<const float4*>(part + (2 * s) * slice)[g];
-      const float4 y = reinterpret_cast<const float4*>(part + (2 * s + 1) * slice)[g];
+    for (int i = 1; i < na; ++i) {
+      const float4 x = reinterpret_cast<const float4*>(part + (2 * i) * slice)[g];
       av.x += x.x; av.y += x.y; av.z += x.z; av.w += x.w;
+    }
+    for (int i = 1; i < nb; ++i) {
+      const float4 y = reinterpret_cast<const float4*>(part + (2 * i + 1) * slice)[g];
       bv.x += y.x; bv.y += y.y; bv.z += y.z; bv.w += y.w;
     }
     uint2 h;
@@ -367,7 +573,7 @@ hipError_t launch_stream(const StreamArgs& in, hipStream_t stream) {
   a.max_tiles = (int)(((int64_t)a.P + (int64_t)a.E * (16 * NJ - 1)) / (16 * NJ));
   if (a.max_tiles <= 0) return hipSuccess;
   const int64_t grid =
-      (int64_t)a.max_tiles * a.splits * (a.N / kFeat) * (MODE == kPerMatrix ? 2 : 1);
+      (int64_t)a.max_tiles * a.splits * (a.N / kFeat);
   hipLaunchKernelGGL((stream_gemm_kernel<NJ, MODE>), dim3((unsigned)grid), dim3(kThreads), 0,
                      stream, a);
   return hipGetLastError();
@@ -408,30 +614,16 @@ int pick_launch(const double* wgs, int n) {
 
 }  // namespace
 
-// K split of the per-matrix W1/W3 launch when `tiles` token tiles hold rows
-// (0 if the shape cannot stream per matrix).  With one workgroup per compute
-// unit every round of workgroups takes as long as its slowest one, even a
-// round that is nearly empty (a lone workgroup streams at one compute unit's
-// rate), and every workgroup pays a fixed cost besides its share of K.
-// Measured at Mixtral shape, T = 8, busy tiles 2..8 and splits 1, 2, 4, the
-// time follows rounds x (1/s + 0.11); the split minimising that is taken,
-// the smaller one on ties.
-constexpr double kSplitFixedCost = 0.11;
-
-int per_matrix_split(int d, int d_ff, double tiles) {
-  const double per = tiles * (d_ff / kFeat);
-  int best = 0;
-  double best_cost = 0.0;
-  for (int s = 1; s <= 64; ++s) {
-    if (!stream_shape_ok(d, d_ff, kWaves, s)) continue;
-    const double rounds = std::ceil(2.0 * s * per / kComputeUnits - 1e-9);
-    const double cost = std::max(rounds, 1.0) * (1.0 / s + kSplitFixedCost);
-    if (best == 0 || cost < best_cost - 1e-12) {
-      best = s;
-      best_cost = cost;
-    }
-  }
-  return best;
+// Partial-sum slices of the per-matrix W1/W3 product (stream_sk_kernel over
+// kComputeUnits workgroups): two for units cut by a workgroup boundary, or
+// the equal pieces of units when there are fewer units than workgroups (most
+// when a single token tile holds rows).
+int sk_slices(int d, int d_ff) {
+  const int cpu = d / kChunkRows;
+  const int U = 2 * (d_ff / kFeat);
+  int s = 1;
+  while (cpu % (2 * s) == 0 && (int64_t)U * 2 * s <= (int64_t)kComputeUnits) s *= 2;
+  return std::max(2, s);
 }
 
 int stream_swiglu_splits(int d, int d_ff, double tiles) {
@@ -448,19 +640,7 @@ int stream_swiglu_splits(int d, int d_ff, double tiles) {
       split[n++] = s;
     }
   const int pick = split[pick_launch(wgs, n)];
-  if (pick == 0) return 0;
-  // per matrix: room for the largest split any busy-tile count may take
-  int most = pick;
-  for (int b = 1; b < kSplitTable; ++b) most = std::max(most, per_matrix_split(d, d_ff, b));
-  return most;
-}
-
-SplitTable stream_split_table(int d, int d_ff, int P, int E) {
-  SplitTable t{};
-  const int max_tiles = std::min((P + E * 15) / 16, kSplitTable - 1);
-  for (int b = 0; b < kSplitTable; ++b)
-    t.split_of[b] = (int8_t)std::max(1, per_matrix_split(d, d_ff, std::min(b, max_tiles)));
-  return t;
+  return pick == 0 ? 0 : sk_slices(d, d_ff);
 }
 
 int stream_down_splits(int d_ff, int d, double tiles) {
@@ -498,9 +678,11 @@ hipError_t launch_stream_swiglu_bf16(const void* x, const int32_t* sorted_token,
     a.splits = 1;
     return launch_stream<1, kFused>(a, stream);
   }
-  const SplitTable tab = stream_split_table(d, d_ff, P, E);
-  for (int b = 0; b < kSplitTable; ++b) a.split_of[b] = tab.split_of[b];
-  return launch_stream<1, kPerMatrix>(a, stream);
+  if (P == 0) return hipSuccess;
+  if (P > kStreamMaxPairs || E > kMaxExperts) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(stream_sk_kernel, dim3((unsigned)kComputeUnits), dim3(kThreads), 0, stream,
+                     a);
+  return hipGetLastError();
 }
 
 hipError_t launch_swiglu_finish_bf16(const float* part, const int32_t* offsets, int P, int d,
@@ -508,9 +690,8 @@ hipError_t launch_swiglu_finish_bf16(const float* part, const int32_t* offsets, 
   const int64_t n4 = (int64_t)P * d_ff / 4;
   if (n4 == 0) return hipSuccess;
   const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 2048);
-  hipLaunchKernelGGL(swiglu_finish_kernel, dim3(blocks), dim3(256), 0, stream, part,
-                     stream_split_table(d, d_ff, P, E), offsets, E, P, d_ff,
-                     static_cast<bf16_t*>(H));
+  hipLaunchKernelGGL(swiglu_finish_kernel, dim3(blocks), dim3(256), 0, stream, part, offsets, E,
+                     P, d_ff, d, (int)kComputeUnits, static_cast<bf16_t*>(H));
   return hipGetLastError();
 }
 

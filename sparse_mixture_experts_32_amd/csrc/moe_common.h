@@ -48,13 +48,6 @@ __device__ __forceinline__ int busy_tiles(const int32_t* __restrict__ offsets, i
   return n;
 }
 
-// K split of the per-matrix small-batch W1/W3 launch for every count of busy
-// 16-row token tiles (index), computed on the host, read by the kernels.
-constexpr int kSplitTable = 72;
-struct SplitTable {
-  int8_t split_of[kSplitTable];
-};
-
 // Locate the token tile `tile` among the experts' segments: expert e owns
 // ceil(count_e / bt) tiles, experts in index order.  Returns false when the
 // tile index is past the last real tile.

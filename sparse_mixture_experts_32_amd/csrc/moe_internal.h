@@ -55,13 +55,12 @@ hipError_t launch_expert_down_f32(const void* H, const ExpertPtrs& W2, const int
 // most 16 rows per token tile), N in tiles of kStreamFeat features.
 constexpr int kStreamFeat = 256;
 // W1/W3 launch when about `tiles` token tiles hold rows: 0 = fused (H written
-// by the product), s >= 1 = one matrix per workgroup with K split up to s
-// ways (fp32 partial sums, completed by launch_swiglu_finish_bf16); -1 if the
-// shape cannot stream.  The per-matrix launch takes its split count from
-// stream_split_table by the number of token tiles that hold rows, which the
-// kernels count from the expert offsets.
+// by the product), s >= 1 = one matrix at a time over a persistent grid that
+// divides the weight rows evenly between the compute units, leaving fp32
+// partial sums in up to s slices per matrix (completed by
+// launch_swiglu_finish_bf16, which reads the expert offsets to know how many
+// each unit has); -1 if the shape cannot stream.
 int stream_swiglu_splits(int d, int d_ff, double tiles);
-SplitTable stream_split_table(int d, int d_ff, int P, int E);
 // W2 K split (slices of O) for about `tiles` busy token tiles; 0 if the
 // shape cannot stream.
 int stream_down_splits(int d_ff, int d, double tiles);

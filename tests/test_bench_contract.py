@@ -41,7 +41,7 @@ def test_roofline_object_is_bytes_over_time_against_the_hbm_peak():
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
     assert r["achieved"] == pytest.approx(a["swiglu_bytes"] / 0.25e-3 / 1e9, rel=1e-4)
     assert r["frac"] == pytest.approx(r["achieved"] / 8000.0, abs=1e-4)
-    assert r["kernel"] == "stream_gemm_kernel<1, 2>"
+    assert r["kernel"] == "stream_sk_kernel"
 
 
 def test_roofline_object_is_flops_over_time_against_the_mfma_peak():
@@ -56,7 +56,7 @@ def test_roofline_object_is_flops_over_time_against_the_mfma_peak():
 
 def test_w1w3_kernel_name_follows_the_plan():
     assert bench.swiglu_kernel(dict(streaming=True, swiglu_splits=0))[0] == "stream_gemm_kernel<1, 1>"
-    assert bench.swiglu_kernel(dict(streaming=True, swiglu_splits=3))[0] == "stream_gemm_kernel<1, 2>"
+    assert bench.swiglu_kernel(dict(streaming=True, swiglu_splits=3))[0] == "stream_sk_kernel"
     assert bench.swiglu_kernel(dict(streaming=False, swiglu_splits=0))[1] == "expert_tiled_bf16.hip"
 
 
