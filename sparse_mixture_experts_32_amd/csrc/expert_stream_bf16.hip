@@ -54,6 +54,13 @@ namespace moe {
 namespace {
 
 struct StreamArgs {
+  // W1/W3 launches of moe_forward: the routing table, from which every
+  // workgroup builds the dispatch tables itself (at most 64 pairs) and
+  // workgroup 0 writes them to offsets / gather / pos_out for the later
+  // kernels; null when the caller passes the tables (gather, offsets)
+  const int32_t* topk_idx;
+  int K;
+  int32_t* pos_out;
   const bf16_t* A;         // [rows, Kdim] activations
   const int32_t* gather;   // sorted_token for gathered rows, else null
   const int32_t* offsets;  // [E + 1]
@@ -130,6 +137,18 @@ struct StreamCfg {
   static constexpr int kKParts = kWaves / kMatsWG;        // waves sharing one matrix
 };
 
+constexpr int kStreamMaxPairs = 64;   // the streaming plan takes T * K <= 64
+
+// Workgroup 0 of a W1/W3 launch that built the dispatch tables writes them
+// out for the finish, W2 and combine kernels (and for the caller).
+__device__ __forceinline__ void publish_route(const StreamArgs& a, const int32_t* off,
+                                              const int32_t* tok, const int32_t* pos) {
+  const int t = threadIdx.x;
+  if (t <= a.E) const_cast<int32_t*>(a.offsets)[t] = off[t];
+  if (t < off[a.E]) const_cast<int32_t*>(a.gather)[t] = tok[t];
+  if (t < a.P) a.pos_out[t] = pos[t];
+}
+
 // One k-step of 32 rows: the 16 loaded weight registers w are transposed
 // into MFMA operands and multiplied with the token operand b.
 //   t: k-rows 0-7 (lanes 0-31) / 8-15 (lanes 32-63); u: 16-23 / 24-31.
@@ -179,8 +198,21 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(StreamArgs a) {
   const int s = bid % a.splits;
   const int ttile = bid / a.splits;
   const int splits = a.splits;
+  // dispatch tables: built here from the routing table, or the caller's
+  __shared__ int32_t sh_off[kMaxExperts + 1];
+  __shared__ int32_t sh_tok[kStreamMaxPairs];
+  __shared__ int32_t sh_pos[kStreamMaxPairs];
+  const int32_t* offsets = a.offsets;
+  const int32_t* gather = a.gather;
+  if (a.topk_idx) {
+    if (threadIdx.x < 64) small_route(a.topk_idx, a.P, a.K, a.E, sh_off, sh_tok, sh_pos);
+    __syncthreads();
+    if (blockIdx.x == 0) publish_route(a, sh_off, sh_tok, sh_pos);
+    offsets = sh_off;
+    gather = sh_tok;
+  }
   int e, row_begin, row_end;
-  if (!find_tile(a.offsets, a.E, 16 * NJ, ttile, e, row_begin, row_end)) return;
+  if (!find_tile(offsets, a.E, 16 * NJ, ttile, e, row_begin, row_end)) return;
   e = __builtin_amdgcn_readfirstlane(e);
   row_begin = __builtin_amdgcn_readfirstlane(row_begin);
   row_end = __builtin_amdgcn_readfirstlane(row_end);
@@ -206,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(StreamArgs a) {
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int r = min(row_begin + j * 16 + (lane & 15), row_end - 1);
-    src_row[j] = a.gather ? a.gather[r] : r;
+    src_row[j] = gather ? gather[r] : r;
   }
 
   // Weight loads are buffer loads: a k-step's 32 rows as one resource (base
@@ -342,7 +374,6 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(StreamArgs a) {
 // before the current piece's epilogue, and the epilogue synchronises the
 // waves through LDS only, so those loads stay in flight across it.
 constexpr int kChunkRows = 2 * 32 * kWaves;
-constexpr int kStreamMaxPairs = 64;   // the streaming plan takes T * K <= 64
 
 __device__ __forceinline__ int sk_small_split(int U, int G, int cpu) {
   int s = 1;
@@ -372,9 +403,16 @@ __global__ __launch_bounds__(kThreads) void stream_sk_kernel(StreamArgs a) {
   // reads come from LDS, not from memory the kernel also writes
   __shared__ int32_t sh_off[kMaxExperts + 1];
   __shared__ int32_t sh_tok[kStreamMaxPairs];
-  if ((int)threadIdx.x <= a.E) sh_off[threadIdx.x] = a.offsets[threadIdx.x];
-  if ((int)threadIdx.x < a.P) sh_tok[threadIdx.x] = a.gather[threadIdx.x];
-  __syncthreads();
+  if (a.topk_idx) {
+    __shared__ int32_t sh_pos[kStreamMaxPairs];
+    if (threadIdx.x < 64) small_route(a.topk_idx, a.P, a.K, a.E, sh_off, sh_tok, sh_pos);
+    __syncthreads();
+    if (blockIdx.x == 0) publish_route(a, sh_off, sh_tok, sh_pos);
+  } else {
+    if ((int)threadIdx.x <= a.E) sh_off[threadIdx.x] = a.offsets[threadIdx.x];
+    if ((int)threadIdx.x < a.P) sh_tok[threadIdx.x] = a.gather[threadIdx.x];
+    __syncthreads();
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tiles_f = a.N / kFeat;
@@ -660,8 +698,13 @@ int stream_down_splits(int d_ff, int d, double tiles) {
 hipError_t launch_stream_swiglu_bf16(const void* x, const int32_t* sorted_token,
                                      const ExpertPtrs& W1, const ExpertPtrs& W3,
                                      const int32_t* offsets, int P, int d, int d_ff, int E,
-                                     int splits, float* part, void* H, hipStream_t stream) {
+                                     int splits, float* part, void* H, const int32_t* topk_idx,
+                                     int K, int32_t* pos, hipStream_t stream) {
+  if (P > kStreamMaxPairs || E > kMaxExperts) return hipErrorInvalidValue;
   StreamArgs a{};
+  a.topk_idx = topk_idx;
+  a.K = K;
+  a.pos_out = pos;
   a.A = static_cast<const bf16_t*>(x);
   a.gather = sorted_token;
   a.offsets = offsets;
@@ -679,7 +722,6 @@ hipError_t launch_stream_swiglu_bf16(const void* x, const int32_t* sorted_token,
     return launch_stream<1, kFused>(a, stream);
   }
   if (P == 0) return hipSuccess;
-  if (P > kStreamMaxPairs || E > kMaxExperts) return hipErrorInvalidValue;
   hipLaunchKernelGGL(stream_sk_kernel, dim3((unsigned)kComputeUnits), dim3(kThreads), 0, stream,
                      a);
   return hipGetLastError();

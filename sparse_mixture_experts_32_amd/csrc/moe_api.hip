@@ -258,15 +258,24 @@ moe_status moe_routing_stats(const int32_t* topk_idx, int64_t T, int32_t E, int3
 
 namespace {
 
+// With `route` (topk_idx, K, pos) the small-batch kernels build the dispatch
+// tables themselves and write them to offsets, sorted_token and pos.
+struct Route {
+  const int32_t* topk_idx = nullptr;
+  int K = 0;
+  int32_t* pos = nullptr;
+};
+
 hipError_t run_swiglu(const Plan& plan, const void* x, const int32_t* sorted_token,
                       const moe::ExpertPtrs& p1, const moe::ExpertPtrs& p3, const int32_t* offsets,
                       int P, int d, int d_ff, int E, int32_t dtype, void* H, void* scratch,
-                      hipStream_t st) {
+                      hipStream_t st, const Route& route = Route()) {
   if (dtype != MOE_BF16)
     return moe::launch_expert_swiglu_f32(x, sorted_token, p1, p3, offsets, P, d, d_ff, E, H, st);
   if (plan.streaming)
     return moe::launch_stream_swiglu_bf16(x, sorted_token, p1, p3, offsets, P, d, d_ff, E,
-                                          plan.swiglu_splits, static_cast<float*>(scratch), H, st);
+                                          plan.swiglu_splits, static_cast<float*>(scratch), H,
+                                          route.topk_idx, route.K, route.pos, st);
   if (moe::tiled_gemm_supported(d, d_ff, true, 1, P))
     return moe::launch_tiled_swiglu_bf16(x, sorted_token, p1, p3, offsets, P, d, d_ff, E, H, st);
   return moe::launch_expert_swiglu_bf16(x, sorted_token, p1, p3, offsets, P, d, d_ff, E, H, st);
@@ -326,11 +335,19 @@ moe_status run_experts(const Plan& plan, const void* x, const moe::ExpertPtrs& p
                        int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K, int32_t dtype,
                        hipStream_t st) {
   const int P = (int)(T * K);
-  hipError_t e = moe::launch_route_permute(b.topk_idx, (int)T, E, K, b.offsets, b.sorted_token,
-                                           b.pos, st);
-  if (e != hipSuccess) return hip_status(e, "route_permute");
+  hipError_t e = hipSuccess;
+  // small batches: the W1/W3 kernels build the dispatch tables themselves
+  Route route;
+  if (plan.streaming) {
+    route.topk_idx = b.topk_idx;
+    route.K = K;
+    route.pos = b.pos;
+  } else {
+    e = moe::launch_route_permute(b.topk_idx, (int)T, E, K, b.offsets, b.sorted_token, b.pos, st);
+    if (e != hipSuccess) return hip_status(e, "route_permute");
+  }
   e = run_swiglu(plan, x, b.sorted_token, p1, p3, b.offsets, P, (int)d, (int)d_ff, E, dtype, b.H,
-                 b.scratch, st);
+                 b.scratch, st, route);
   if (e != hipSuccess) return hip_status(e, "expert_swiglu");
   if (plan.swiglu_splits > 0) {
     e = moe::launch_swiglu_finish_bf16(static_cast<const float*>(b.scratch), b.offsets, P,

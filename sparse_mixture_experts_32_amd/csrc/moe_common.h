@@ -48,6 +48,30 @@ __device__ __forceinline__ int busy_tiles(const int32_t* __restrict__ offsets, i
   return n;
 }
 
+// The dispatch tables of a small batch (P <= 64 pairs, E <= 64 experts),
+// built by the calling wavefront: the stable counting sort of the dispatch
+// kernel (pair p = t K + r routed to expert e goes to offsets[e] + #{p' < p :
+// idx[p'] = e}); a pair whose index lies outside [0, E) is dropped, pos = -1.
+// off[E + 1], tok[P] (token of each sorted position) and pos[P] may be LDS
+// or global memory.
+__device__ __forceinline__ void small_route(const int32_t* __restrict__ topk_idx, int P, int K,
+                                            int E, int32_t* off, int32_t* tok, int32_t* pos) {
+  const int lane = threadIdx.x & 63;
+  int e = lane < P ? topk_idx[lane] : -1;
+  if (e >= E) e = -1;
+  const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int dest = -1, total = 0;
+  for (int x = 0; x < E; ++x) {
+    const uint64_t m = __ballot(e == x);
+    if (e == x) dest = total + __popcll(m & lower);
+    if (lane == 0) off[x] = total;
+    total += __popcll(m);
+  }
+  if (lane == 0) off[E] = total;
+  if (dest >= 0) tok[dest] = lane / K;
+  if (lane < P) pos[lane] = dest;
+}
+
 // Locate the token tile `tile` among the experts' segments: expert e owns
 // ceil(count_e / bt) tiles, experts in index order.  Returns false when the
 // tile index is past the last real tile.

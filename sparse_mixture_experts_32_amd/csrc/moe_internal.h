@@ -64,10 +64,15 @@ int stream_swiglu_splits(int d, int d_ff, double tiles);
 // W2 K split (slices of O) for about `tiles` busy token tiles; 0 if the
 // shape cannot stream.
 int stream_down_splits(int d_ff, int d, double tiles);
+// With topk_idx non-null the kernels build the dispatch tables themselves
+// from the routing table and write offsets, sorted_token and pos (so no
+// dispatch launch is needed); otherwise they read the caller's offsets and
+// sorted_token.
 hipError_t launch_stream_swiglu_bf16(const void* x, const int32_t* sorted_token,
                                      const ExpertPtrs& W1, const ExpertPtrs& W3,
                                      const int32_t* offsets, int P, int d, int d_ff, int E,
-                                     int splits, float* part, void* H, hipStream_t stream);
+                                     int splits, float* part, void* H, const int32_t* topk_idx,
+                                     int K, int32_t* pos, hipStream_t stream);
 // H[r][f] = bf16(SiLU(sum_s part[s][0][r][f]) * sum_s part[s][1][r][f]), over
 // the splits the W1/W3 launch took.
 hipError_t launch_swiglu_finish_bf16(const float* part, const int32_t* offsets, int P, int d,
