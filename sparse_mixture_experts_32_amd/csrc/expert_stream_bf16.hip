@@ -477,11 +477,17 @@ __global__ __launch_bounds__(kThreads) void stream_sk_kernel(StreamArgs a) {
   u32x4_t b0[NJ], b1[NJ];
 
   // weight rows of k-step `step` of a piece: a zero-size resource when the
-  // piece is empty, so the loads return zeros without a memory access
+  // piece is empty, so the loads return zeros without a memory access.  The
+  // address and size are wave-uniform, but the compiler cannot see it through
+  // the loop-carried piece and would wrap every load in a loop over distinct
+  // resources; readfirstlane puts the resource in scalar registers.
   auto load_w = [&](u32x4_t (&wr)[kLoads], const char* base, int step, bool live) {
+    const uint64_t addr = reinterpret_cast<uint64_t>(base) + (uint64_t)step * 32 * row_bytes;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+    const int size = __builtin_amdgcn_readfirstlane(live ? 32 * (int)row_bytes : 0);
     const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(base) + (int64_t)step * 32 * row_bytes, (short)0,
-        live ? 32 * (int)row_bytes : 0, kBufferWord3);
+        reinterpret_cast<char*>(((uint64_t)hi << 32) | lo), (short)0, size, kBufferWord3);
 #pragma unroll
     for (int r = 0; r < kLoads; ++r) {
       const int row = (r & 7) + 16 * (r >> 3);
