@@ -358,22 +358,23 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(StreamArgs a) {
 //
 // Work units are (busy token tile, feature tile of 256, matrix), numbered
 // u = (tile * tiles_f + ftile) * 2 + matrix, each K = Kdim rows long and cut
-// into chunks of kChunkRows rows (two k-steps per wave).  With G workgroups
+// into chunks of kChunkRows rows (one k-step per wave).  With G workgroups
 // (one per compute unit):
 //   * U >= G units: workgroup w takes chunks [w C / G, (w+1) C / G) of the
 //     C = U * (Kdim / kChunkRows) chunks in unit order, so every workgroup
-//     streams the same number of weight bytes and no round of workgroups is
-//     left nearly empty.  A unit is cut at most once; its head piece goes
-//     to partial-sum slice 0, its tail to slice 1.
+//     streams the same number of weight bytes (to one chunk: for
+//     Mixtral's shapes at 8 tokens, 49 chunks each) and no round of
+//     workgroups is left nearly empty.  A unit is cut at most once; its head
+//     piece goes to partial-sum slice 0, its tail to slice 1.
 //   * U < G: every unit is cut into the same number s of pieces (the largest
 //     power of two with U s <= G dividing the chunk count), piece i to
 //     slice i.
-// Inside a piece the eight waves split its rows evenly, as in the per-matrix
-// launch (a whole-unit piece sums exactly as that launch's unsplit product).
+// Inside a piece the eight waves split its rows evenly (one chunk's k-step
+// each per chunk) and their partial products meet in LDS in wave order.
 // The weight and token loads of the next piece's first k-step are issued
 // before the current piece's epilogue, and the epilogue synchronises the
 // waves through LDS only, so those loads stay in flight across it.
-constexpr int kChunkRows = 2 * 32 * kWaves;
+constexpr int kChunkRows = 32 * kWaves;
 
 __device__ __forceinline__ int sk_small_split(int U, int G, int cpu) {
   int s = 1;
@@ -442,7 +443,7 @@ __global__ __launch_bounds__(kThreads) void stream_sk_kernel(StreamArgs a) {
   struct Piece {
     const char* wbase;      // this wave's first weight row of the piece
     const bf16_t* bsrc;     // this lane's token row at the wave's first k
-    int nsteps;             // k-steps of 32 rows per wave (0: no piece)
+    int nsteps;             // k-steps of 32 rows per wave, one per chunk (0: no piece)
     int row_begin, row_end, f0, mat, slice;
     int64_t next;           // first chunk after the piece
   };
@@ -515,9 +516,12 @@ __global__ __launch_bounds__(kThreads) void stream_sk_kernel(StreamArgs a) {
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[h][c][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // Steps go in pairs; after an odd count the second of the last pair
+    // loads zeros (zero-size resource) against the piece's last token step,
+    // so it adds exactly nothing and reads no memory past the piece.
     for (int i = 0; i < cur.nsteps; i += 2) {
-      load_w(w1, cur.wbase, i + 1, true);
-      load_b(b1, cur.bsrc + (i + 1) * 32);
+      load_w(w1, cur.wbase, i + 1, i + 1 < cur.nsteps);
+      load_b(b1, cur.bsrc + min(i + 1, cur.nsteps - 1) * 32);
       mma_step<NJ>(w0, b0, acc);
       // k-step i + 2: this piece's, or the next piece's first
       const bool inside = i + 2 < cur.nsteps;
