@@ -62,8 +62,10 @@ class Layer:
         self.plan = M.plan_for(T, d, d_ff, E, K, M.BF16)
         self.H = torch.empty((P, d_ff), dtype=torch.bfloat16, device=dev)
         self.O = torch.empty((self.plan["down_splits"], P, d), dtype=torch.float32, device=dev)
-        self.scratch = torch.empty(max(self.plan["swiglu_scratch_bytes"], 16), dtype=torch.uint8,
-                                   device=dev)
+        # one scratch for the W1/W3 partial sums and the W2 tail pieces (used in turn)
+        self.scratch = torch.empty(max(self.plan["swiglu_scratch_bytes"],
+                                       self.plan["down_scratch_bytes"], 16),
+                                   dtype=torch.uint8, device=dev)
         self.y = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
         self.ws = torch.empty(M.workspace_size(T, d, d_ff, E, K, M.BF16), dtype=torch.uint8,
                               device=dev)
@@ -88,7 +90,7 @@ class Layer:
         M.moe_swiglu_finish(self.scratch, w.T, w.d, w.d_ff, w.E, w.K, M.BF16, self.offsets,
                             self.H)
         mark(4)
-        M.moe_expert_down(self.H, self.W2, w.T, w.K, self.offsets, self.O)
+        M.moe_expert_down(self.H, self.W2, w.T, w.K, self.offsets, self.O, scratch=self.scratch)
         mark(5)
         M.moe_combine(self.O, self.topk_w, self.pos, self.y)
         mark(6)

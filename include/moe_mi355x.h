@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 #define MOE_MAX_EXPERTS 64
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -69,6 +69,11 @@ typedef struct moe_plan {
   int32_t down_splits;          /* K splits of the W2 product = slices of O             */
   size_t swiglu_scratch_bytes;  /* fp32 partial sums the W1/W3 product needs (0 if none) */
   int32_t streaming;            /* 1: weight-streaming (small batch) kernels, 0: tiled   */
+  size_t down_scratch_bytes;    /* fp32 partial sums the W2 product needs (0 if none):  */
+                                /* large batches run whole-K tiles for the complete     */
+                                /* rounds of compute units and cut the tiles of the     */
+                                /* last round into K pieces, summed into O by the same  */
+                                /* call (down_splits is then 1)                         */
 } moe_plan;
 
 /* Index of each intermediate inside the workspace; see moe_workspace_layout. */
@@ -80,7 +85,7 @@ typedef enum {
   MOE_WS_POS = 4,          /* int32 [T, K]   sorted position of pair (t, r)         */
   MOE_WS_H = 5,            /* dtype [T*K, d_ff]  SwiGLU product, expert-sorted rows */
   MOE_WS_O = 6,            /* float [down_splits, T*K, d]  expert outputs (slices)  */
-  MOE_WS_SCRATCH = 7,      /* swiglu_scratch_bytes of fp32 partial sums             */
+  MOE_WS_SCRATCH = 7,      /* max(swiglu_, down_scratch_bytes) of fp32 partial sums */
   MOE_WS_COUNT = 8
 } moe_ws_item;
 
@@ -234,11 +239,16 @@ moe_status moe_swiglu_finish(const void* scratch, int64_t T, int64_t d, int64_t 
  * Step 7 (code block D, second line): O_s[r] = H[r, k-slice s] W2[e][k-slice s]
  * for every sorted row r of expert e and every split s < plan.down_splits,
  * fp32 accumulation.  O float [plan.down_splits, T*K, d]; the sum over s is
- * taken by moe_combine.
+ * taken by moe_combine.  scratch: device buffer of plan.down_scratch_bytes
+ * (may be NULL when that is 0; MOE_EWORKSPACE if smaller), which may be the
+ * buffer given to moe_expert_swiglu: with down_scratch_bytes > 0 the call
+ * keeps the K pieces of its last round of tiles there and adds them into O
+ * (in piece order) before it returns.
  */
 moe_status moe_expert_down(const void* H, const void* const* W2, int64_t T, int64_t d,
                            int64_t d_ff, int32_t E, int32_t K, int32_t dtype,
-                           const int32_t* offsets, float* O, void* stream);
+                           const int32_t* offsets, float* O, void* scratch, size_t scratch_bytes,
+                           void* stream);
 
 /*
  * Step 8 (section 2.1.1 sum; code block E, zero-initialised accumulator):

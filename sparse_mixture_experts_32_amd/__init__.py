@@ -27,7 +27,7 @@ __all__ = [
     "moe_expert_down",
     "moe_combine", "moe_rmsnorm", "moe_stack_forward", "EXPORTED_SYMBOLS",
     "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "moe_routing_stats",
-    "stack_workspace_size",
+    "stack_workspace_size", "ABI_VERSION",
     "swa_workspace_size", "swa_attention", "swa_cache_append",
 ]
 
@@ -66,9 +66,13 @@ _c_p = ctypes.c_void_p
 _c_sz = ctypes.c_size_t
 
 
+ABI_VERSION = 4   # MOE_ABI_VERSION of include/moe_mi355x.h that this binding speaks
+
+
 class _Plan(ctypes.Structure):
     _fields_ = [("swiglu_splits", ctypes.c_int32), ("down_splits", ctypes.c_int32),
-                ("swiglu_scratch_bytes", ctypes.c_size_t), ("streaming", ctypes.c_int32)]
+                ("swiglu_scratch_bytes", ctypes.c_size_t), ("streaming", ctypes.c_int32),
+                ("down_scratch_bytes", ctypes.c_size_t)]
 
 
 def load_library(path: str | None = None):
@@ -105,7 +109,7 @@ def load_library(path: str | None = None):
         "moe_swiglu_finish": (_c_i32, [_c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_p,
                                        _c_p, _c_p]),
         "moe_expert_down": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
-                                     _c_p, _c_p, _c_p]),
+                                     _c_p, _c_p, _c_p, _c_sz, _c_p]),
         "moe_combine": (_c_i32, [_c_p, _c_i32, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_p, _c_i32,
                                  _c_i32, _c_p]),
         "moe_rmsnorm": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, ctypes.c_float, _c_i32, _c_p]),
@@ -125,6 +129,11 @@ def load_library(path: str | None = None):
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    if lib.moe_abi_version() != ABI_VERSION:
+        raise MoeLibraryMissing(
+            "%s speaks C ABI version %d, this binding version %d; rebuild it with "
+            "`python -m sparse_mixture_experts_32_amd.build`" % (path, lib.moe_abi_version(),
+                                                                ABI_VERSION))
     if path == library_path():
         _lib = lib
     return lib
@@ -170,7 +179,8 @@ def plan_for(T, d, d_ff, E, K, dtype) -> dict:
     p = _Plan()
     _check(lib.moe_plan_for(T, d, d_ff, E, K, dtype, ctypes.byref(p)), lib)
     return dict(swiglu_splits=p.swiglu_splits, down_splits=p.down_splits,
-                swiglu_scratch_bytes=p.swiglu_scratch_bytes, streaming=bool(p.streaming))
+                swiglu_scratch_bytes=p.swiglu_scratch_bytes, streaming=bool(p.streaming),
+                down_scratch_bytes=p.down_scratch_bytes)
 
 
 def workspace_size(T, d, d_ff, E, K, dtype) -> int:
@@ -332,17 +342,24 @@ def moe_swiglu_finish(scratch, T, d, d_ff, E, K, dtype, offsets, H, stream=None)
     return H
 
 
-def moe_expert_down(H, W2, T, K, offsets, O=None, stream=None):
-    """O has shape [down_splits, T*K, d] (see plan_for)."""
+def moe_expert_down(H, W2, T, K, offsets, O=None, scratch=None, stream=None):
+    """O has shape [down_splits, T*K, d] (see plan_for).  scratch: at least
+    plan_for(...)["down_scratch_bytes"] bytes (allocated here when None)."""
     lib = load_library()
     E = len(W2)
     d_ff, d = W2[0].shape
     dt = _dtype_code(H)
+    plan = plan_for(T, d, d_ff, E, K, dt) if T else None
     if O is None:
-        S = plan_for(T, d, d_ff, E, K, dt)["down_splits"] if T else 1
+        S = plan["down_splits"] if T else 1
         O = torch.empty((S, T * K, d), dtype=torch.float32, device=H.device)
+    need = plan["down_scratch_bytes"] if T else 0
+    if scratch is None and need:
+        scratch = torch.empty(need, dtype=torch.uint8, device=H.device)
     _check(lib.moe_expert_down(_ptr(H), _ptr_array(W2), T, d, d_ff, E, K, dt,
-                               _ptr(offsets), _ptr(O), _stream(stream)), lib)
+                               _ptr(offsets), _ptr(O), _ptr(scratch),
+                               scratch.numel() if scratch is not None else 0, _stream(stream)),
+           lib)
     return O
 
 

@@ -40,6 +40,7 @@
 //   * tile order: each XCD runs a contiguous range in which 4 feature tiles
 //     are interleaved with the token tiles, so the ~32 workgroups it runs at
 //     once share a few weight tiles and a few token tiles in its L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "moe_common.h"
@@ -78,7 +79,51 @@ struct TiledArgs {
   int max_tiles;
   int splits;              // K splits (one output slice each; 1 for W1/W3)
   int group_f;             // feature tiles interleaved in the tile order (divides N / feat)
+  // W2 with a tail split (null: none): partial sums of the tail pieces,
+  // side_rows rows of [256] floats per piece, side_pieces pieces
+  float* side;
+  int side_rows;
+  int side_pieces;
 };
+
+// A W2 launch with a tail split numbers the busy tiles densely, p = 0 ..
+// nt-1 over the bt busy token tiles (group_f feature tiles interleaved with
+// the token tiles, as the plain order).  The first Nw tiles, whole rounds of
+// kTailRound workgroups, run over all of K and write O directly; the last nt
+// - Nw (the partial round) are cut into S pieces along K, dispatched last,
+// whose fp32 partial sums tail_fixup_kernel adds in piece order into O.  So
+// the chip's last round holds S times as many, S times shorter workgroups
+// instead of a few long ones, and O needs one slice.
+constexpr int kTailRound = 256;   // compute units
+
+__device__ __forceinline__ void tail_plan(const int32_t* offsets, int E, int tiles_f, int Kdim,
+                                          int side_pieces, int& bt, int& nt, int& Nw, int& S) {
+  bt = busy_tiles(offsets, E, 256);
+  nt = bt * tiles_f;
+  const int rem = nt % kTailRound;
+  const int cap = min(kTailRound, side_pieces);
+  const int quads = Kdim / (kBK * kSlots);   // a piece takes a multiple of kSlots stages
+  S = 1;
+  for (int s = 8; s >= 2; --s)
+    if (quads % s == 0 && rem * s <= cap) {
+      S = s;
+      break;
+    }
+  Nw = S > 1 ? nt - rem : nt;
+}
+
+__device__ __forceinline__ void tail_tile(int p, int bt, int gf, int& ftile, int& ttile) {
+  ftile = (p / (gf * bt)) * gf + p % gf;
+  ttile = (p / gf) % bt;
+}
+
+// Feature tiles interleaved in the tile order: the largest divisor of
+// tiles_f up to kGroupF.
+int group_for(int tiles_f) {
+  int g = kGroupF;
+  while (tiles_f % g != 0) --g;
+  return g;
+}
 
 // Chunk swizzles (16-byte chunks): weight rows hold 32 chunks, token rows 4.
 __device__ __forceinline__ int swz_w(int r) { return 2 * (r & 3) + 8 * ((r >> 3) & 1); }
@@ -129,16 +174,39 @@ __global__ __launch_bounds__(128 * kWavesT) void tiled_gemm_kernel(TiledArgs arg
   // the token tiles (feature fastest), so the ~32 workgroups an XCD runs at
   // once span a few weight tiles and a few token tiles and both operands are
   // reused from that XCD's L2.
-  const int G = gridDim.x;
-  const int v = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
   const int tiles_f = args.N / C::kFeat;
-  const int per_split = args.max_tiles * tiles_f;
-  const int split = v / per_split;
-  if (split >= args.splits) return;
-  const int w = v % per_split;
   const int gf = args.group_f;
-  const int ftile = (w / (gf * args.max_tiles)) * gf + w % gf;
-  const int ttile = (w / gf) % args.max_tiles;
+  int split = 0, nsplit = args.splits, ftile, ttile;
+  int piece = -1;  // index of a tail piece in args.side, or -1
+  if (!DUAL && args.side) {
+    int bt, nt, Nw, S;
+    tail_plan(args.offsets, args.E, tiles_f, args.Kdim, args.side_pieces, bt, nt, Nw, S);
+    const int Gw = (Nw + 7) / 8 * 8;
+    const int b = blockIdx.x;
+    int p;
+    if (b < Gw) {
+      const int v = (b % 8) * (Gw / 8) + b / 8;
+      if (v >= Nw) return;
+      p = v;
+      nsplit = 1;
+    } else {
+      piece = b - Gw;
+      if (piece >= (nt - Nw) * S) return;
+      p = Nw + piece / S;
+      split = piece % S;
+      nsplit = S;
+    }
+    tail_tile(p, bt, gf, ftile, ttile);
+  } else {
+    const int G = gridDim.x;
+    const int v = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+    const int per_split = args.max_tiles * tiles_f;
+    split = v / per_split;
+    if (split >= args.splits) return;
+    const int w = v % per_split;
+    ftile = (w / (gf * args.max_tiles)) * gf + w % gf;
+    ttile = (w / gf) % args.max_tiles;
+  }
   int e, row_begin, row_end;
   if (!find_tile(args.offsets, args.E, BT, ttile, e, row_begin, row_end)) return;
 
@@ -185,7 +253,7 @@ __global__ __launch_bounds__(128 * kWavesT) void tiled_gemm_kernel(TiledArgs arg
   }
   const int64_t wstep = (int64_t)kBK * N * 2;   // bytes per stage along k
   const int astep = kBK * 2;
-  const int ksplit = args.Kdim / args.splits;    // this split's k-range
+  const int ksplit = args.Kdim / nsplit;        // this split's k-range
   const char* abase = reinterpret_cast<const char*>(args.A) + (int64_t)split * ksplit * 2;
 #pragma unroll
   for (int u = 0; u < C::kWInstr; ++u) wbase[u] += (int64_t)split * ksplit * N * 2;
@@ -361,6 +429,14 @@ __global__ __launch_bounds__(128 * kWavesT) void tiled_gemm_kernel(TiledArgs arg
         v2.y = pack_bf16x2(silu_f32(a[2]) * bb[2], silu_f32(a[3]) * bb[3]);
         *reinterpret_cast<uint2*>(static_cast<bf16_t*>(args.out) + (int64_t)r * N + f) = v2;
       }
+    } else if (piece >= 0) {
+      // tail piece: fp32 partial sums of the tile, row r - row_begin
+      float* dst = args.side + ((int64_t)piece * args.side_rows + (r - row_begin)) * kBF;
+#pragma unroll
+      for (int i = 0; i < C::kMI; ++i) {
+        const f32x4_t a = acc[i][jb];
+        *reinterpret_cast<float4*>(dst + wf * 128 + i * 16 + fq) = make_float4(a[0], a[1], a[2], a[3]);
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < C::kMI; ++i) {
@@ -380,16 +456,54 @@ hipError_t launch_tiled(const TiledArgs& in, int P, hipStream_t stream) {
   a.max_tiles = (int)(((int64_t)P + (int64_t)a.E * (BT - 1)) / BT);
   if (a.max_tiles <= 0) return hipSuccess;
   const int tiles_f = a.N / C::kFeat;
-  a.group_f = kGroupF;
-  while (tiles_f % a.group_f != 0) --a.group_f;
+  a.group_f = group_for(tiles_f);
   int64_t blocks = (int64_t)a.max_tiles * tiles_f * a.splits;
   blocks = (blocks + 7) / 8 * 8;  // whole XCD rounds for the remapped order
+  if (a.side) blocks += kTailRound;   // the tail pieces, after the whole tiles
   hipLaunchKernelGGL((tiled_gemm_kernel<BT, DUAL>), dim3((unsigned)blocks),
                      dim3(C::kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
+// O rows of the tail tiles of a split W2 launch: the sum of the tile's S
+// pieces in piece order.  One block per (tail tile, 4 rows), a thread per 4
+// features.
+__global__ __launch_bounds__(256) void tail_fixup_kernel(const float* __restrict__ side,
+                                                         int side_rows, int side_pieces,
+                                                         const int32_t* __restrict__ offsets,
+                                                         int E, int N, int Kdim, int group_f,
+                                                         float* __restrict__ O) {
+  constexpr int kRowsPerBlock = 256 / (kBF / 4);
+  const int tiles_f = N / kBF;
+  int bt, nt, Nw, S;
+  tail_plan(offsets, E, tiles_f, Kdim, side_pieces, bt, nt, Nw, S);
+  const int blocks_per_tile = (side_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int t = blockIdx.x / blocks_per_tile;   // tail tile
+  if (S == 1 || t >= nt - Nw) return;
+  const int i = (blockIdx.x % blocks_per_tile) * kRowsPerBlock + threadIdx.x / (kBF / 4);
+  const int c = (threadIdx.x % (kBF / 4)) * 4;
+  int ftile, ttile, e, rb, re;
+  tail_tile(Nw + t, bt, group_f, ftile, ttile);
+  if (!find_tile(offsets, E, 256, ttile, e, rb, re) || i >= min(256, re - rb)) return;
+  const float* src = side + ((int64_t)t * S * side_rows + i) * kBF + c;
+  float4 a = *reinterpret_cast<const float4*>(src);
+  for (int q = 1; q < S; ++q) {
+    const float4 x = *reinterpret_cast<const float4*>(src + (int64_t)q * side_rows * kBF);
+    a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+  }
+  *reinterpret_cast<float4*>(O + (int64_t)(rb + i) * N + ftile * kBF + c) = a;
+}
+
 }  // namespace
+
+size_t tiled_down_side_bytes(int P, int d, int d_ff) {
+  // only where even the fewest busy token tiles P rows fill (one per 256)
+  // make a whole round of W2 tiles; 256 pieces of min(256, P) rows x 256
+  // fp32 features
+  if (P <= 0 || !tiled_gemm_supported(d_ff, d, false, 1, P)) return 0;
+  if ((int64_t)((P + 255) / 256) * (d / kBF) < kTailRound) return 0;
+  return (size_t)kTailRound * std::min(256, P) * kBF * sizeof(float);
+}
 
 bool tiled_gemm_supported(int Kdim, int N, bool dual, int splits, int64_t a_rows) {
   // token-operand byte offsets are 32-bit per lane
@@ -423,8 +537,15 @@ hipError_t launch_tiled_swiglu_bf16(const void* x, const int32_t* sorted_token,
 
 hipError_t launch_tiled_down_bf16(const void* H, const ExpertPtrs& W2, const int32_t* offsets,
                                   int P, int d, int d_ff, int E, int splits, float* O,
-                                  hipStream_t stream) {
+                                  float* side, size_t side_bytes, hipStream_t stream) {
   TiledArgs a{};
+  if (side && side_bytes > 0 && P > 0 && splits == 1) {
+    a.side = side;
+    a.side_rows = std::min(256, P);
+    a.side_pieces =
+        (int)std::min<size_t>(kTailRound, side_bytes / ((size_t)a.side_rows * kBF * 4));
+    if (a.side_pieces < 2) a.side = nullptr;
+  }
   a.A = static_cast<const bf16_t*>(H);
   a.gather = nullptr;
   a.offsets = offsets;
@@ -437,6 +558,19 @@ hipError_t launch_tiled_down_bf16(const void* H, const ExpertPtrs& W2, const int
   a.P = P;
   a.splits = splits;
   return launch_tiled<256, false>(a, P, stream);
+}
+
+hipError_t launch_tiled_down_fixup(const float* side, size_t side_bytes, const int32_t* offsets,
+                                   int P, int d, int d_ff, int E, float* O, hipStream_t stream) {
+  if (!side || side_bytes == 0 || P <= 0) return hipSuccess;
+  const int rows = std::min(256, P);
+  const int pieces = (int)std::min<size_t>(kTailRound, side_bytes / ((size_t)rows * kBF * 4));
+  if (pieces < 2) return hipSuccess;
+  // at most kTailRound / 2 tail tiles (two pieces or more each)
+  const int blocks = kTailRound / 2 * ((rows + 3) / 4);
+  hipLaunchKernelGGL(tail_fixup_kernel, dim3(blocks), dim3(256), 0, stream, side, rows, pieces,
+                     offsets, E, d, d_ff, group_for(d / kBF), O);
+  return hipGetLastError();
 }
 
 }  // namespace moe

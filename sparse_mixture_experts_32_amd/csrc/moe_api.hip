@@ -70,7 +70,8 @@ moe_status check_shape(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K,
 struct Plan {
   int swiglu_splits = 0;
   int down_splits = 1;
-  size_t scratch = 0;
+  size_t scratch = 0;        // W1/W3 partial sums
+  size_t down_scratch = 0;   // W2 tail pieces
   bool streaming = false;
 };
 
@@ -83,7 +84,10 @@ Plan make_plan(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K, int32_t
   const int64_t P = T * K;
   if (dt != MOE_BF16 || P == 0) return p;
   if (P > 64) {
-    if (moe::tiled_gemm_supported((int)d_ff, (int)d, false, 1, P)) {
+    // W2 of at least a whole round of tiles: whole-K tiles and a split tail
+    // (one slice of O); smaller: K splits so that the grid fills the chip
+    p.down_scratch = moe::tiled_down_side_bytes((int)P, (int)d, (int)d_ff);
+    if (p.down_scratch == 0 && moe::tiled_gemm_supported((int)d_ff, (int)d, false, 1, P)) {
       const int64_t tiles = moe::tiled_gemm_tiles((int)P, E, (int)d, false);
       for (int s = 2; s <= 4 && tiles * (s - 1) < 4 * 256; ++s)
         if (moe::tiled_gemm_supported((int)d_ff, (int)d, false, s, P)) p.down_splits = s;
@@ -122,7 +126,7 @@ void layout(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K, int32_t dt
   put(MOE_WS_POS, P * 4);
   put(MOE_WS_H, P * (size_t)d_ff * dtype_bytes(dt));
   put(MOE_WS_O, (size_t)plan.down_splits * P * (size_t)d * 4);
-  put(MOE_WS_SCRATCH, plan.scratch);
+  put(MOE_WS_SCRATCH, std::max(plan.scratch, plan.down_scratch));
   *total = o;
 }
 
@@ -190,6 +194,7 @@ moe_status moe_plan_for(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K
   plan->swiglu_splits = p.swiglu_splits;
   plan->down_splits = p.down_splits;
   plan->swiglu_scratch_bytes = p.scratch;
+  plan->down_scratch_bytes = p.down_scratch;
   plan->streaming = p.streaming ? 1 : 0;
   return ok();
 }
@@ -283,12 +288,18 @@ hipError_t run_swiglu(const Plan& plan, const void* x, const int32_t* sorted_tok
 
 hipError_t run_down(const Plan& plan, const void* H, const moe::ExpertPtrs& p2,
                     const int32_t* offsets, int P, int d, int d_ff, int E, int32_t dtype, float* O,
-                    hipStream_t st) {
+                    void* scratch, hipStream_t st) {
   if (dtype != MOE_BF16) return moe::launch_expert_down_f32(H, p2, offsets, P, d, d_ff, E, O, st);
   if (plan.streaming)
     return moe::launch_stream_down_bf16(H, p2, offsets, P, d, d_ff, E, plan.down_splits, O, st);
-  if (moe::tiled_gemm_supported(d_ff, d, false, plan.down_splits, P))
-    return moe::launch_tiled_down_bf16(H, p2, offsets, P, d, d_ff, E, plan.down_splits, O, st);
+  if (moe::tiled_gemm_supported(d_ff, d, false, plan.down_splits, P)) {
+    float* side = plan.down_scratch ? static_cast<float*>(scratch) : nullptr;
+    hipError_t e = moe::launch_tiled_down_bf16(H, p2, offsets, P, d, d_ff, E, plan.down_splits,
+                                               O, side, plan.down_scratch, st);
+    if (e == hipSuccess && side)
+      e = moe::launch_tiled_down_fixup(side, plan.down_scratch, offsets, P, d, d_ff, E, O, st);
+    return e;
+  }
   return moe::launch_expert_down_bf16(H, p2, offsets, P, d, d_ff, E, O, st);
 }
 
@@ -354,7 +365,7 @@ moe_status run_experts(const Plan& plan, const void* x, const moe::ExpertPtrs& p
                                        (int)d, (int)d_ff, E, b.H, st);
     if (e != hipSuccess) return hip_status(e, "swiglu_finish");
   }
-  e = run_down(plan, b.H, p2, b.offsets, P, (int)d, (int)d_ff, E, dtype, b.O, st);
+  e = run_down(plan, b.H, p2, b.offsets, P, (int)d, (int)d_ff, E, dtype, b.O, b.scratch, st);
   if (e != hipSuccess) return hip_status(e, "expert_down");
   return MOE_OK;
 }
@@ -407,7 +418,8 @@ moe_status moe_swiglu_finish(const void* scratch, int64_t T, int64_t d, int64_t 
 
 moe_status moe_expert_down(const void* H, const void* const* W2, int64_t T, int64_t d,
                            int64_t d_ff, int32_t E, int32_t K, int32_t dtype,
-                           const int32_t* offsets, float* O, void* stream) {
+                           const int32_t* offsets, float* O, void* scratch, size_t scratch_bytes,
+                           void* stream) {
   moe_status s = check_shape(T, d, d_ff, E, K, dtype);
   if (s) return s;
   if (T == 0) return ok();
@@ -418,8 +430,14 @@ moe_status moe_expert_down(const void* H, const void* const* W2, int64_t T, int6
   moe::ExpertPtrs p2;
   if ((s = fill_ptrs(W2, E, p2, "W2", bf16))) return s;
   const Plan plan = make_plan(T, d, d_ff, E, K, dtype);
+  if (plan.down_scratch > 0) {
+    if (!scratch || scratch_bytes < plan.down_scratch)
+      return fail(MOE_EWORKSPACE, "scratch has %zu bytes, needs %zu", scratch ? scratch_bytes : 0,
+                  plan.down_scratch);
+    if (!aligned16(scratch)) return fail(MOE_EWORKSPACE, "scratch must be 16-byte aligned");
+  }
   return finish(run_down(plan, H, p2, offsets, (int)(T * K), (int)d, (int)d_ff, E, dtype, O,
-                         (hipStream_t)stream),
+                         scratch, (hipStream_t)stream),
                 "expert_down");
 }
 

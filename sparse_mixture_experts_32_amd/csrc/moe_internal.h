@@ -91,9 +91,16 @@ hipError_t launch_tiled_swiglu_bf16(const void* x, const int32_t* sorted_token,
                                     const ExpertPtrs& W1, const ExpertPtrs& W3,
                                     const int32_t* offsets, int P, int d, int d_ff, int E,
                                     void* H, hipStream_t stream);
+// With `side` (tiled_down_side_bytes bytes, splits == 1) the W2 launch runs
+// whole tiles for its complete rounds of compute units and cuts the tiles of
+// its last, partial round into K pieces whose fp32 partial sums land in
+// `side`; launch_tiled_down_fixup then writes their O rows.  O has one slice.
+size_t tiled_down_side_bytes(int P, int d, int d_ff);
 hipError_t launch_tiled_down_bf16(const void* H, const ExpertPtrs& W2, const int32_t* offsets,
                                   int P, int d, int d_ff, int E, int splits, float* O,
-                                  hipStream_t stream);
+                                  float* side, size_t side_bytes, hipStream_t stream);
+hipError_t launch_tiled_down_fixup(const float* side, size_t side_bytes, const int32_t* offsets,
+                                   int P, int d, int d_ff, int E, float* O, hipStream_t stream);
 
 // Lets `kernel` use `bytes` of dynamic LDS on the current device (once per
 // device and kernel).

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4 == M.ABI_VERSION
     assert lib.moe_status_str(0) == b"MOE_OK"
     assert lib.moe_status_str(4) == b"MOE_EHIP"
 
@@ -59,9 +59,15 @@ def test_plan(lib):
     assert p["swiglu_scratch_bytes"] == p["swiglu_splits"] * 2 * 16 * 14336 * 4
     p = M.plan_for(32, 4096, 14336, 8, 2, M.BF16)     # fused W1/W3: H written directly
     assert p["streaming"] and p["swiglu_splits"] == 0 and p["swiglu_scratch_bytes"] == 0
+    # 4096 tokens fill at least 32 x 16 W2 tiles (two rounds of 256 compute
+    # units): whole-K tiles with a split last round, one slice of O, 256
+    # pieces of 256 rows x 256 fp32 features
     p = M.plan_for(4096, 4096, 14336, 8, 2, M.BF16)
     assert not p["streaming"] and p["swiglu_splits"] == 0 and p["swiglu_scratch_bytes"] == 0
-    assert p["down_splits"] >= 1 and 14336 % (128 * p["down_splits"]) == 0
+    assert p["down_splits"] == 1 and p["down_scratch_bytes"] == 256 * 256 * 256 * 4
+    # 512 tokens (at least 4 x 16 tiles): K splits, no scratch
+    p = M.plan_for(512, 4096, 14336, 8, 2, M.BF16)
+    assert p["down_splits"] > 1 and p["down_scratch_bytes"] == 0
     # the tiled W2 kernel addresses its token operand (H) with 32-bit byte
     # offsets: at d_ff = 65536, 32000 rows fit (K split 4), 33000 do not and
     # W2 falls back to the unsplit grouped kernel
@@ -185,7 +191,14 @@ def test_stage_entry_points_validate(lib):
     # the streaming plan of an 8-token Mixtral-shape layer needs scratch
     assert lib.moe_expert_swiglu(FAKE, arr, arr, 8, 4096, 14336, 8, 2, 1, FAKE, FAKE, FAKE,
                                  None, 0, None) == EWORKSPACE
-    assert lib.moe_expert_down(FAKE, arr, 4, 128, 256, 8, 2, 1, FAKE, None, None) == EINVAL
+    assert lib.moe_expert_down(FAKE, arr, 4, 128, 256, 8, 2, 1, FAKE, None, None, 0,
+                               None) == EINVAL
+    # a 4096-token Mixtral-shape W2 product keeps the pieces of its last round
+    # of tiles in scratch: refused before any launch without it, or too small
+    assert lib.moe_expert_down(FAKE, arr, 4096, 4096, 14336, 8, 2, 1, FAKE, FAKE, None, 0,
+                               None) == EWORKSPACE
+    assert lib.moe_expert_down(FAKE, arr, 4096, 4096, 14336, 8, 2, 1, FAKE, FAKE, FAKE, 1 << 20,
+                               None) == EWORKSPACE
     assert lib.moe_combine(FAKE, 1, FAKE, FAKE, 4, 128, 0, FAKE2, 0, 0, None) == EINVAL
     assert lib.moe_combine(FAKE, 1, FAKE, FAKE, 4, 128, 2, None, 0, 0, None) == EINVAL
     assert lib.moe_combine(FAKE, 0, FAKE, FAKE, 4, 128, 2, FAKE2, 0, 0, None) == EINVAL

@@ -357,10 +357,12 @@ def test_empty_batch(dev):
 
 
 # (640, 256, 384): tiled; (8, 1024, 1024): per-matrix streaming W1/W3 +
-# finish; (16, 768, 2048): fused streaming W1/W3
-@pytest.mark.parametrize("T,d,d_ff", [(640, 256, 384), (8, 1024, 1024), (16, 768, 2048)])
-def test_deterministic_and_stages_match_forward(dev, T, d, d_ff):
-    w = small(T=T, d=d, d_ff=d_ff)
+# finish; (16, 768, 2048): fused streaming W1/W3; (130, 49152, 1024) over 3
+# experts: tiled W2 with its last round of tiles split along K (576 tiles)
+@pytest.mark.parametrize("T,d,d_ff,E", [(640, 256, 384, 8), (8, 1024, 1024, 8),
+                                        (16, 768, 2048, 8), (130, 49152, 1024, 3)])
+def test_deterministic_and_stages_match_forward(dev, T, d, d_ff, E):
+    w = small(T=T, d=d, d_ff=d_ff, E=E)
     say("determinism", T, d, d_ff, M.plan_for(T, d, d_ff, w.E, w.K, M.BF16))
     inp = W.layer_inputs(w, dev)
     y1, v1 = run_forward(inp, 2)
@@ -473,6 +475,26 @@ def test_tiled_operand_past_32_bit_offsets_takes_grouped_kernels(dev):
     assert late.size > 0
     tokens = np.concatenate([late[:: max(1, late.size // 8)][:8], [0, w.T - 1]])
     check_layer(inp, w.K, tokens=np.unique(tokens), bf16_store=False)
+
+
+def test_w2_split_tail_every_row(dev):
+    """A W2 product of at least one whole round of tiles.  d = 49152 gives 192
+    feature tiles of 256 columns; 130 tokens top-2 over 3 experts fill 3
+    token tiles (at most 130 rows each), 576 tiles in all: 512 run over the
+    whole of K, and the 64 of the last, partial round are cut into 4 K pieces
+    whose sums the fix-up adds.  Every token is checked against the oracle."""
+    w = small(T=130, d=49152, d_ff=1024, E=3)
+    plan = M.plan_for(w.T, w.d, w.d_ff, w.E, w.K, M.BF16)
+    say("W2 split tail", w.T, w.d, w.d_ff, w.E, plan)
+    assert not plan["streaming"] and plan["down_splits"] == 1 and plan["down_scratch_bytes"] > 0
+    inp = W.layer_inputs(w, dev)
+    _, v = run_forward(inp, w.K)
+    counts = np.diff(v["offsets"].cpu().numpy())
+    tiles = int(np.sum((counts + 255) // 256)) * (w.d // 256)
+    say("expert rows", counts.tolist(), "tiles", tiles)
+    assert tiles % 256 != 0 and tiles > 256           # a whole round and a split tail
+    del v
+    check_layer(inp, w.K)
 
 
 def test_full_T512_sampled(dev):
