@@ -57,12 +57,15 @@ typedef const __attribute__((address_space(1))) void global_void_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kBF = 256;       // weight columns per workgroup
+constexpr int kBF = 256;       // weight columns per workgroup (W2; W1/W3 may take 512)
 constexpr int kBK = 32;        // k per stage
 constexpr int kSlots = 4;      // LDS ring depth
-constexpr int kWavesT = 4;     // waves along tokens (x 2 along weight columns)
 constexpr int kGroupF = 4;     // feature tiles interleaved in the tile order
-constexpr int kRowBytesW = kBF * 2;   // 512
+// W1/W3 takes the 128 x 512 tile up to this average of rows per expert.
+// Measured at Mixtral shape, 8 experts: 7.5-11 % faster layers at 128-384
+// tokens, 3.4 % slower at 512 (three of the eight experts then hold more than
+// 128 rows and take a second, nearly empty tile).
+constexpr int kWideRowsPerExpert = 112;
 constexpr int kRowBytesA = kBK * 2;   // 64
 
 struct TiledArgs {
@@ -145,25 +148,32 @@ __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
 }
 
-template <int BT, bool DUAL>
+// BT tokens x BF weight columns per workgroup: eight waves of 128 columns x
+// 64 tokens, BF / 128 along the columns and the rest along the tokens.
+template <int BT, bool DUAL, int BF>
 struct TiledCfg {
-  static constexpr int kWaves = 2 * kWavesT;   // 2 along weight columns x 4 along tokens
+  static constexpr int kWaves = 8;
   static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kWavesF = BF / 128;     // along weight columns
+  static constexpr int kWavesT = kWaves / kWavesF;
   static constexpr int kWT = BT / kWavesT;     // tokens per wave
   static constexpr int kNJ = kWT / 16;
   static constexpr int kMI = 8;                // 128 weight columns per wave
-  static constexpr int kSlotW = kBK * kRowBytesW;  // 16 KB
+  static constexpr int kSlotW = kBK * BF * 2;      // 16 KB at BF = 256
   static constexpr int kSlotA = BT * kRowBytesA;   // 16 KB at BT = 256
-  static constexpr int kWInstr = kSlotW / 1024 / kWaves;  // per wave per stage
+  static constexpr int kInstrW = kSlotW / 1024;    // 1 KB load instructions per stage
+  static constexpr int kWInstr = kInstrW / kWaves;  // per wave per stage
   static constexpr int kAInstr = kSlotA / 1024 / kWaves;
   static constexpr int kDmaPerStage = kWInstr + kAInstr;
-  static constexpr int kFeat = DUAL ? kBF / 2 : kBF;
+  static constexpr int kFeat = DUAL ? BF / 2 : BF;
+  static_assert(kWT == 64, "every wave holds 128 x 64");
   static_assert(kSlotA % (1024 * kWaves) == 0 && kSlotW % (1024 * kWaves) == 0, "copy split");
+  static_assert(kSlots * (kSlotW + kSlotA) <= 160 * 1024, "LDS");
 };
 
-template <int BT, bool DUAL>
-__global__ __launch_bounds__(128 * kWavesT) void tiled_gemm_kernel(TiledArgs args) {
-  using C = TiledCfg<BT, DUAL>;
+template <int BT, bool DUAL, int BF>
+__global__ __launch_bounds__(512) void tiled_gemm_kernel(TiledArgs args) {
+  using C = TiledCfg<BT, DUAL, BF>;
   __shared__ __align__(1024) char sW0[C::kSlotW], sW1[C::kSlotW], sW2[C::kSlotW], sW3[C::kSlotW];
   __shared__ __align__(1024) char sA0[C::kSlotA], sA1[C::kSlotA], sA2[C::kSlotA], sA3[C::kSlotA];
   char* const sW[kSlots] = {sW0, sW1, sW2, sW3};
@@ -213,8 +223,8 @@ __global__ __launch_bounds__(128 * kWavesT) void tiled_gemm_kernel(TiledArgs arg
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int wf = wave & 1;
-  const int wt = wave >> 1;
+  const int wf = wave % C::kWavesF;
+  const int wt = wave / C::kWavesF;
   const int64_t N = args.N;
   const int fbase = ftile * C::kFeat;
   (void)tid;
@@ -225,7 +235,7 @@ __global__ __launch_bounds__(128 * kWavesT) void tiled_gemm_kernel(TiledArgs arg
   // 1024 / kRowB consecutive rows of one sub-tile, so its source matrix is
   // uniform and the address is a scalar base plus a 32-bit lane offset.
   constexpr int kSub = DUAL ? 2 : 1;
-  constexpr int kSubCols = kBF / kSub;
+  constexpr int kSubCols = BF / kSub;
   constexpr int kRowB = kSubCols * 2;          // bytes per LDS row of a sub-tile
   constexpr int kChunks = kRowB / 16;          // 16-byte chunks per row
   constexpr int kRowsPerInstr = 1024 / kRowB;
@@ -233,9 +243,9 @@ __global__ __launch_bounds__(128 * kWavesT) void tiled_gemm_kernel(TiledArgs arg
   const char* wbase[C::kWInstr];
 #pragma unroll
   for (int u = 0; u < C::kWInstr; ++u) {
-    const int ii = wave * C::kWInstr + u;                 // 0 .. 15
-    const int sub = ii / (16 / kSub);
-    const int r = (ii % (16 / kSub)) * kRowsPerInstr + lane / kChunks;
+    const int ii = wave * C::kWInstr + u;                 // 0 .. kInstrW - 1
+    const int sub = ii / (C::kInstrW / kSub);
+    const int r = (ii % (C::kInstrW / kSub)) * kRowsPerInstr + lane / kChunks;
     const int c = (lane % kChunks) ^ swz_w(r);
     wbase[u] = static_cast<const char*>(sub == 0 ? args.Wa.p[e] : args.Wb.p[e]);
     woff[u] = (uint32_t)(((int64_t)r * N + fbase + 8 * c) * 2);
@@ -431,7 +441,7 @@ __global__ __launch_bounds__(128 * kWavesT) void tiled_gemm_kernel(TiledArgs arg
       }
     } else if (piece >= 0) {
       // tail piece: fp32 partial sums of the tile, row r - row_begin
-      float* dst = args.side + ((int64_t)piece * args.side_rows + (r - row_begin)) * kBF;
+      float* dst = args.side + ((int64_t)piece * args.side_rows + (r - row_begin)) * BF;
 #pragma unroll
       for (int i = 0; i < C::kMI; ++i) {
         const f32x4_t a = acc[i][jb];
@@ -449,9 +459,9 @@ __global__ __launch_bounds__(128 * kWavesT) void tiled_gemm_kernel(TiledArgs arg
   }
 }
 
-template <int BT, bool DUAL>
+template <int BT, bool DUAL, int BF>
 hipError_t launch_tiled(const TiledArgs& in, int P, hipStream_t stream) {
-  using C = TiledCfg<BT, DUAL>;
+  using C = TiledCfg<BT, DUAL, BF>;
   TiledArgs a = in;
   a.max_tiles = (int)(((int64_t)P + (int64_t)a.E * (BT - 1)) / BT);
   if (a.max_tiles <= 0) return hipSuccess;
@@ -460,7 +470,7 @@ hipError_t launch_tiled(const TiledArgs& in, int P, hipStream_t stream) {
   int64_t blocks = (int64_t)a.max_tiles * tiles_f * a.splits;
   blocks = (blocks + 7) / 8 * 8;  // whole XCD rounds for the remapped order
   if (a.side) blocks += kTailRound;   // the tail pieces, after the whole tiles
-  hipLaunchKernelGGL((tiled_gemm_kernel<BT, DUAL>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((tiled_gemm_kernel<BT, DUAL, BF>), dim3((unsigned)blocks),
                      dim3(C::kThreads), 0, stream, a);
   return hipGetLastError();
 }
@@ -532,7 +542,14 @@ hipError_t launch_tiled_swiglu_bf16(const void* x, const int32_t* sorted_token,
   a.E = E;
   a.P = P;
   a.splits = 1;
-  return launch_tiled<256, true>(a, P, stream);
+  // 128 tokens x 512 columns (256 features of each matrix) while the experts
+  // average at most kWideRowsPerExpert rows: each stage loads 32 KB of
+  // weights against 8 KB of tokens instead of 16 against 16 (a compute unit's
+  // load rate is shared by both), and the weight rows come in 512-byte
+  // segments instead of 256
+  if (d_ff % 256 == 0 && (int64_t)P <= (int64_t)kWideRowsPerExpert * E)
+    return launch_tiled<128, true, 512>(a, P, stream);
+  return launch_tiled<256, true, 256>(a, P, stream);
 }
 
 hipError_t launch_tiled_down_bf16(const void* H, const ExpertPtrs& W2, const int32_t* offsets,
@@ -557,7 +574,7 @@ hipError_t launch_tiled_down_bf16(const void* H, const ExpertPtrs& W2, const int
   a.E = E;
   a.P = P;
   a.splits = splits;
-  return launch_tiled<256, false>(a, P, stream);
+  return launch_tiled<256, false, 256>(a, P, stream);
 }
 
 hipError_t launch_tiled_down_fixup(const float* side, size_t side_bytes, const int32_t* offsets,
