@@ -61,11 +61,14 @@ constexpr int kBF = 256;       // weight columns per workgroup (W2; W1/W3 may ta
 constexpr int kBK = 32;        // k per stage
 constexpr int kSlots = 4;      // LDS ring depth
 constexpr int kGroupF = 4;     // feature tiles interleaved in the tile order
-// W1/W3 takes the 128 x 512 tile up to this average of rows per expert.
-// Measured at Mixtral shape, 8 experts: 7.5-11 % faster layers at 128-384
-// tokens, 3.4 % slower at 512 (three of the eight experts then hold more than
-// 128 rows and take a second, nearly empty tile).
-constexpr int kWideRowsPerExpert = 112;
+// W1/W3 chooses the tile shape per expert (tiled_mixed_kernel) up to this
+// average of rows per expert.  Against 256 x 256 tiles throughout, at Mixtral
+// shape with 8 experts (one box, 3 A/B pairs): 5.6, 7.3, 10.3, 11.2 and
+// 5.7 % faster layers at 64, 128, 256, 384 and 512 tokens, level at 640 and
+// 768.  (The 128 x 512 tile for every expert was 3.4 % slower at 512 tokens:
+// three of the eight experts then hold more than 128 rows and would take a
+// second, nearly empty tile.)
+constexpr int kMixedRowsPerExpert = 192;
 constexpr int kRowBytesA = kBK * 2;   // 64
 
 struct TiledArgs {
@@ -171,55 +174,16 @@ struct TiledCfg {
   static_assert(kSlots * (kSlotW + kSlotA) <= 160 * 1024, "LDS");
 };
 
+// One (token tile, feature tile, k-range) of a grouped product: the rows
+// row_begin .. min(row_end, row_begin + BT) - 1 of expert e, features
+// ftile * kFeat .., K slice `split` of `nsplit` (a tail piece of W2 when piece
+// >= 0).  sW / sA: the four LDS slots of the weight and token operands.
 template <int BT, bool DUAL, int BF>
-__global__ __launch_bounds__(512) void tiled_gemm_kernel(TiledArgs args) {
+__device__ __forceinline__ void tile_body(const TiledArgs& args, char* const (&sW)[kSlots],
+                                          char* const (&sA)[kSlots], int e, int row_begin,
+                                          int row_end, int ftile, int split, int nsplit,
+                                          int piece) {
   using C = TiledCfg<BT, DUAL, BF>;
-  __shared__ __align__(1024) char sW0[C::kSlotW], sW1[C::kSlotW], sW2[C::kSlotW], sW3[C::kSlotW];
-  __shared__ __align__(1024) char sA0[C::kSlotA], sA1[C::kSlotA], sA2[C::kSlotA], sA3[C::kSlotA];
-  char* const sW[kSlots] = {sW0, sW1, sW2, sW3};
-  char* const sA[kSlots] = {sA0, sA1, sA2, sA3};
-
-  // Tile order.  Workgroup b runs on XCD b % 8; each XCD gets a contiguous
-  // range of the order, in which group_f feature tiles are interleaved with
-  // the token tiles (feature fastest), so the ~32 workgroups an XCD runs at
-  // once span a few weight tiles and a few token tiles and both operands are
-  // reused from that XCD's L2.
-  const int tiles_f = args.N / C::kFeat;
-  const int gf = args.group_f;
-  int split = 0, nsplit = args.splits, ftile, ttile;
-  int piece = -1;  // index of a tail piece in args.side, or -1
-  if (!DUAL && args.side) {
-    int bt, nt, Nw, S;
-    tail_plan(args.offsets, args.E, tiles_f, args.Kdim, args.side_pieces, bt, nt, Nw, S);
-    const int Gw = (Nw + 7) / 8 * 8;
-    const int b = blockIdx.x;
-    int p;
-    if (b < Gw) {
-      const int v = (b % 8) * (Gw / 8) + b / 8;
-      if (v >= Nw) return;
-      p = v;
-      nsplit = 1;
-    } else {
-      piece = b - Gw;
-      if (piece >= (nt - Nw) * S) return;
-      p = Nw + piece / S;
-      split = piece % S;
-      nsplit = S;
-    }
-    tail_tile(p, bt, gf, ftile, ttile);
-  } else {
-    const int G = gridDim.x;
-    const int v = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
-    const int per_split = args.max_tiles * tiles_f;
-    split = v / per_split;
-    if (split >= args.splits) return;
-    const int w = v % per_split;
-    ftile = (w / (gf * args.max_tiles)) * gf + w % gf;
-    ttile = (w / gf) % args.max_tiles;
-  }
-  int e, row_begin, row_end;
-  if (!find_tile(args.offsets, args.E, BT, ttile, e, row_begin, row_end)) return;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -460,6 +424,121 @@ __global__ __launch_bounds__(512) void tiled_gemm_kernel(TiledArgs args) {
 }
 
 template <int BT, bool DUAL, int BF>
+__global__ __launch_bounds__(512) void tiled_gemm_kernel(TiledArgs args) {
+  using C = TiledCfg<BT, DUAL, BF>;
+  __shared__ __align__(1024) char sW0[C::kSlotW], sW1[C::kSlotW], sW2[C::kSlotW], sW3[C::kSlotW];
+  __shared__ __align__(1024) char sA0[C::kSlotA], sA1[C::kSlotA], sA2[C::kSlotA], sA3[C::kSlotA];
+  char* const sW[kSlots] = {sW0, sW1, sW2, sW3};
+  char* const sA[kSlots] = {sA0, sA1, sA2, sA3};
+
+  // Tile order.  Workgroup b runs on XCD b % 8; each XCD gets a contiguous
+  // range of the order, in which group_f feature tiles are interleaved with
+  // the token tiles (feature fastest), so the ~32 workgroups an XCD runs at
+  // once span a few weight tiles and a few token tiles and both operands are
+  // reused from that XCD's L2.
+  const int tiles_f = args.N / C::kFeat;
+  const int gf = args.group_f;
+  int split = 0, nsplit = args.splits, ftile, ttile;
+  int piece = -1;  // index of a tail piece in args.side, or -1
+  if (!DUAL && args.side) {
+    int bt, nt, Nw, S;
+    tail_plan(args.offsets, args.E, tiles_f, args.Kdim, args.side_pieces, bt, nt, Nw, S);
+    const int Gw = (Nw + 7) / 8 * 8;
+    const int b = blockIdx.x;
+    int p;
+    if (b < Gw) {
+      const int v = (b % 8) * (Gw / 8) + b / 8;
+      if (v >= Nw) return;
+      p = v;
+      nsplit = 1;
+    } else {
+      piece = b - Gw;
+      if (piece >= (nt - Nw) * S) return;
+      p = Nw + piece / S;
+      split = piece % S;
+      nsplit = S;
+    }
+    tail_tile(p, bt, gf, ftile, ttile);
+  } else {
+    const int G = gridDim.x;
+    const int v = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+    const int per_split = args.max_tiles * tiles_f;
+    split = v / per_split;
+    if (split >= args.splits) return;
+    const int w = v % per_split;
+    ftile = (w / (gf * args.max_tiles)) * gf + w % gf;
+    ttile = (w / gf) % args.max_tiles;
+  }
+  int e, row_begin, row_end;
+  if (!find_tile(args.offsets, args.E, BT, ttile, e, row_begin, row_end)) return;
+
+  tile_body<BT, DUAL, BF>(args, sW, sA, e, row_begin, row_end, ftile, split, nsplit, piece);
+}
+
+// W1/W3 with a tile shape per expert: experts of at most 128 rows take one
+// 128 x 512 tile (256 features of each matrix) per feature tile, larger
+// experts 256 x 256 tiles.  The units of each shape are numbered as the
+// plain order numbers tiles (group_f feature tiles interleaved with the
+// token tiles).  Workgroup b runs on XCD b % 8, and XCD x takes its equal
+// share of the wide units first (the longer ones), then its share of the
+// 256-row units, so the XCDs stay balanced and each reuses a few weight and
+// token tiles from its L2.  The four 40 KB LDS slots hold either shape.
+constexpr int kMixedSlot = 40 * 1024;
+
+__global__ __launch_bounds__(512) void tiled_mixed_kernel(TiledArgs args) {
+  __shared__ __align__(1024) char s0[kMixedSlot], s1[kMixedSlot], s2[kMixedSlot], s3[kMixedSlot];
+  using CW = TiledCfg<128, true, 512>;
+  using CS = TiledCfg<256, true, 256>;
+  const int tiles_fw = args.N / CW::kFeat;
+  const int tiles_fs = args.N / CS::kFeat;
+  // wide experts (1 .. 128 rows) and 256-row token tiles of the others
+  int nw = 0, ns = 0;
+  for (int x = 0; x < args.E; ++x) {
+    const int c = args.offsets[x + 1] - args.offsets[x];
+    if (c > 0 && c <= 128) ++nw;
+    else ns += (c + 255) / 256;
+  }
+  const int NW = nw * tiles_fw, NS = ns * tiles_fs;
+  const int xcd = blockIdx.x % 8, l = blockIdx.x / 8;
+  const int w0 = xcd * NW / 8, wn = (xcd + 1) * NW / 8 - w0;
+  const int s0i = xcd * NS / 8, sn = (xcd + 1) * NS / 8 - s0i;
+  const bool wide = l < wn;
+  int u;
+  if (wide) u = w0 + l;
+  else if (l < wn + sn) u = s0i + (l - wn);
+  else return;
+  const int gf = args.group_f;   // divides tiles_fw and tiles_fs
+  const int nt = wide ? nw : ns;
+  const int ftile = (u / (gf * nt)) * gf + u % gf;
+  int tt = (u / gf) % nt;        // the tt-th wide expert, or 256-row tile of the others
+  int e = 0, row_begin = 0;
+  for (; e < args.E; ++e) {
+    const int b = args.offsets[e];
+    const int c = args.offsets[e + 1] - b;
+    const bool ew = c > 0 && c <= 128;
+    if (wide && ew) {
+      if (tt == 0) { row_begin = b; break; }
+      --tt;
+    } else if (!wide && !ew) {
+      const int tiles = (c + 255) / 256;
+      if (tt < tiles) { row_begin = b + 256 * tt; break; }
+      tt -= tiles;
+    }
+  }
+  if (e == args.E) return;   // not reached for a unit below NW + NS
+  const int row_end = args.offsets[e + 1];
+  if (wide) {
+    char* const sW[kSlots] = {s0, s1, s2, s3};
+    char* const sA[kSlots] = {s0 + CW::kSlotW, s1 + CW::kSlotW, s2 + CW::kSlotW, s3 + CW::kSlotW};
+    tile_body<128, true, 512>(args, sW, sA, e, row_begin, row_end, ftile, 0, 1, -1);
+  } else {
+    char* const sW[kSlots] = {s0, s1, s2, s3};
+    char* const sA[kSlots] = {s0 + CS::kSlotW, s1 + CS::kSlotW, s2 + CS::kSlotW, s3 + CS::kSlotW};
+    tile_body<256, true, 256>(args, sW, sA, e, row_begin, row_end, ftile, 0, 1, -1);
+  }
+}
+
+template <int BT, bool DUAL, int BF>
 hipError_t launch_tiled(const TiledArgs& in, int P, hipStream_t stream) {
   using C = TiledCfg<BT, DUAL, BF>;
   TiledArgs a = in;
@@ -542,13 +621,22 @@ hipError_t launch_tiled_swiglu_bf16(const void* x, const int32_t* sorted_token,
   a.E = E;
   a.P = P;
   a.splits = 1;
-  // 128 tokens x 512 columns (256 features of each matrix) while the experts
-  // average at most kWideRowsPerExpert rows: each stage loads 32 KB of
-  // weights against 8 KB of tokens instead of 16 against 16 (a compute unit's
-  // load rate is shared by both), and the weight rows come in 512-byte
-  // segments instead of 256
-  if (d_ff % 256 == 0 && (int64_t)P <= (int64_t)kWideRowsPerExpert * E)
-    return launch_tiled<128, true, 512>(a, P, stream);
+  // Experts of at most 128 rows take 128 tokens x 512 columns (256 features
+  // of each matrix): each stage loads 32 KB of weights against 8 KB of tokens
+  // instead of 16 against 16 (a compute unit's load rate is shared by both),
+  // and the weight rows come in 512-byte segments instead of 256.
+  if (d_ff % 256 == 0 && (int64_t)P <= (int64_t)kMixedRowsPerExpert * E) {
+    const int tiles_fs = d_ff / TiledCfg<256, true, 256>::kFeat;
+    a.group_f = group_for(tiles_fs / 2);   // divides both feature-tile counts
+    // at most E wide experts of tiles_fs / 2 units, and the 256-row tiles of
+    // the others (at most max_tiles) of tiles_fs units; 8 extra for the
+    // XCD shares' rounding
+    const int64_t max_tiles = ((int64_t)P + (int64_t)E * 255) / 256;
+    const int64_t units = (int64_t)E * (tiles_fs / 2) + max_tiles * tiles_fs;
+    const int64_t blocks = (units + 7) / 8 * 8 + 16;
+    hipLaunchKernelGGL(tiled_mixed_kernel, dim3((unsigned)blocks), dim3(512), 0, stream, a);
+    return hipGetLastError();
+  }
   return launch_tiled<256, true, 256>(a, P, stream);
 }
 
