@@ -213,12 +213,15 @@ CSRC = os.path.join(ROOT, "sparse_mixture_experts_32_amd", "csrc")
 def swiglu_kernel(plan):
     """(kernel name as the profiler prints it, source file) of the W1/W3
     stage: the streaming kernel in its fused form, the per-matrix streaming
-    kernel over a persistent grid, or the tiled kernel."""
+    kernel over a persistent grid, the tiled kernel with a tile shape per
+    expert, or the tiled kernel with 256 x 256 tiles."""
     if plan["streaming"]:
         if plan["swiglu_splits"] == 0:
             return "stream_gemm_kernel<1, 1>", "expert_stream_bf16.hip"
         return "stream_sk_kernel", "expert_stream_bf16.hip"
-    return "tiled_gemm_kernel<256, true>", "expert_tiled_bf16.hip"
+    if plan.get("swiglu_mixed"):
+        return "tiled_mixed_kernel", "expert_tiled_bf16.hip"
+    return "tiled_gemm_kernel<256, true, 256>", "expert_tiled_bf16.hip"
 
 
 def measured_traffic(workload, plan):

@@ -74,6 +74,9 @@ typedef struct moe_plan {
                                 /* rounds of compute units and cut the tiles of the     */
                                 /* last round into K pieces, summed into O by the same  */
                                 /* call (down_splits is then 1)                         */
+  int32_t swiglu_mixed;         /* 1: the tiled W1/W3 product picks its tile shape per  */
+                                /* expert: 128 tokens x 512 columns for experts of at   */
+                                /* most 128 rows, 256 x 256 for the others              */
 } moe_plan;
 
 /* Index of each intermediate inside the workspace; see moe_workspace_layout. */

@@ -585,6 +585,10 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(const float* __restrict
 
 }  // namespace
 
+bool tiled_swiglu_mixed(int P, int E, int d_ff) {
+  return d_ff % 256 == 0 && (int64_t)P <= (int64_t)kMixedRowsPerExpert * E;
+}
+
 size_t tiled_down_side_bytes(int P, int d, int d_ff) {
   // only where even the fewest busy token tiles P rows fill (one per 256)
   // make a whole round of W2 tiles; 256 pieces of min(256, P) rows x 256
@@ -625,7 +629,7 @@ hipError_t launch_tiled_swiglu_bf16(const void* x, const int32_t* sorted_token,
   // of each matrix): each stage loads 32 KB of weights against 8 KB of tokens
   // instead of 16 against 16 (a compute unit's load rate is shared by both),
   // and the weight rows come in 512-byte segments instead of 256.
-  if (d_ff % 256 == 0 && (int64_t)P <= (int64_t)kMixedRowsPerExpert * E) {
+  if (tiled_swiglu_mixed(P, E, d_ff)) {
     const int tiles_fs = d_ff / TiledCfg<256, true, 256>::kFeat;
     a.group_f = group_for(tiles_fs / 2);   // divides both feature-tile counts
     // at most E wide experts of tiles_fs / 2 units, and the 256-row tiles of

@@ -73,6 +73,7 @@ struct Plan {
   size_t scratch = 0;        // W1/W3 partial sums
   size_t down_scratch = 0;   // W2 tail pieces
   bool streaming = false;
+  bool swiglu_mixed = false;  // tiled W1/W3 with a tile shape per expert
 };
 
 // Batches whose expert segments fit one 16-row token tile per expert in the
@@ -87,6 +88,8 @@ Plan make_plan(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K, int32_t
     // W2 of at least a whole round of tiles: whole-K tiles and a split tail
     // (one slice of O); smaller: K splits so that the grid fills the chip
     p.down_scratch = moe::tiled_down_side_bytes((int)P, (int)d, (int)d_ff);
+    p.swiglu_mixed = moe::tiled_gemm_supported((int)d, (int)d_ff, true, 1, P) &&
+                     moe::tiled_swiglu_mixed((int)P, E, (int)d_ff);
     if (p.down_scratch == 0 && moe::tiled_gemm_supported((int)d_ff, (int)d, false, 1, P)) {
       const int64_t tiles = moe::tiled_gemm_tiles((int)P, E, (int)d, false);
       for (int s = 2; s <= 4 && tiles * (s - 1) < 4 * 256; ++s)
@@ -195,6 +198,7 @@ moe_status moe_plan_for(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K
   plan->down_splits = p.down_splits;
   plan->swiglu_scratch_bytes = p.scratch;
   plan->down_scratch_bytes = p.down_scratch;
+  plan->swiglu_mixed = p.swiglu_mixed ? 1 : 0;
   plan->streaming = p.streaming ? 1 : 0;
   return ok();
 }

@@ -87,6 +87,9 @@ hipError_t launch_stream_down_bf16(const void* H, const ExpertPtrs& W2, const in
 // 32 bits, else the grouped kernels of expert_gemm_bf16.hip take the product.
 bool tiled_gemm_supported(int Kdim, int N, bool dual, int splits, int64_t a_rows);
 int tiled_gemm_tiles(int P, int E, int N, bool dual);  // worst-case workgroups per split
+// Whether the tiled W1/W3 launch chooses its tile shape per expert (128 x 512
+// for experts of at most 128 rows, 256 x 256 otherwise).
+bool tiled_swiglu_mixed(int P, int E, int d_ff);
 hipError_t launch_tiled_swiglu_bf16(const void* x, const int32_t* sorted_token,
                                     const ExpertPtrs& W1, const ExpertPtrs& W3,
                                     const int32_t* offsets, int P, int d, int d_ff, int E,

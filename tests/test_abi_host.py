@@ -65,9 +65,13 @@ def test_plan(lib):
     p = M.plan_for(4096, 4096, 14336, 8, 2, M.BF16)
     assert not p["streaming"] and p["swiglu_splits"] == 0 and p["swiglu_scratch_bytes"] == 0
     assert p["down_splits"] == 1 and p["down_scratch_bytes"] == 256 * 256 * 256 * 4
-    # 512 tokens (at least 4 x 16 tiles): K splits, no scratch
+    assert not p["swiglu_mixed"]
+    # 512 tokens (at least 4 x 16 tiles): K splits, no scratch; W1/W3 picks
+    # its tile shape per expert (at most 192 rows per expert on average)
     p = M.plan_for(512, 4096, 14336, 8, 2, M.BF16)
-    assert p["down_splits"] > 1 and p["down_scratch_bytes"] == 0
+    assert p["down_splits"] > 1 and p["down_scratch_bytes"] == 0 and p["swiglu_mixed"]
+    assert not M.plan_for(1024, 4096, 14336, 8, 2, M.BF16)["swiglu_mixed"]
+    assert not M.plan_for(512, 4096, 14208, 8, 2, M.BF16)["swiglu_mixed"]   # d_ff % 256
     # the tiled W2 kernel addresses its token operand (H) with 32-bit byte
     # offsets: at d_ff = 65536, 32000 rows fit (K split 4), 33000 do not and
     # W2 falls back to the unsplit grouped kernel
