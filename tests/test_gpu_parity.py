@@ -497,6 +497,48 @@ def test_w2_split_tail_every_row(dev):
     check_layer(inp, w.K)
 
 
+@pytest.mark.parametrize("counts", [(0, 1, 128, 129, 256, 257, 100, 153),
+                                    (512, 0, 0, 0, 0, 0, 0, 512),
+                                    (128,) * 8])
+def test_tile_shape_per_expert_boundaries(dev, counts):
+    """The W1/W3 product with a tile shape per expert (128 x 512 tiles for
+    experts of at most 128 rows, 256 x 256 otherwise) and the K-split W2
+    product, on routing built by hand: experts of 0, 1, 128, 129, 256 and 257
+    rows; only 256-row tiles; only the wide shape.  Token i takes the experts
+    of entries i and i + T of the sorted label list (distinct, since no
+    expert holds T or more pairs).  Each expert's output rows (the W2 slices
+    summed) are compared with the oracle's expert on the same token rows."""
+    E, K = len(counts), 2
+    P = sum(counts)
+    T = P // K
+    w = small(T=T, d=256, d_ff=512, E=E)
+    plan = M.plan_for(T, w.d, w.d_ff, E, K, M.BF16)
+    say("tile shape per expert", counts, plan)
+    assert plan["swiglu_mixed"] and not plan["streaming"]
+    labels = np.repeat(np.arange(E), counts)
+    idx_np = np.stack([labels[:T], labels[T:]], axis=1).astype(np.int32)
+    assert np.all(idx_np[:, 0] != idx_np[:, 1])
+    inp = W.layer_inputs(w, dev)
+    off, st, pos = M.moe_route_permute(torch.from_numpy(idx_np).to(dev), E)
+    H = M.moe_expert_swiglu(inp["x"], inp["W1"], inp["W3"], K, off, st)
+    Ob = M.moe_expert_down(H, inp["W2"], T, K, off)
+    torch.cuda.synchronize()
+    r_counts, r_off, r_st, _, r_pos = O.route_tables(idx_np, E)
+    assert off.cpu().numpy().tolist() == list(r_off)
+    assert st.cpu().numpy().tolist() == list(r_st)
+    o_sum = PY.to_np(Ob).sum(axis=0)     # [splits, P, d]: the slices' sum
+    x = PY.to_np(inp["x"])
+    W1s, W3s, W2s = LazyNp(inp["W1"]), LazyNp(inp["W3"]), LazyNp(inp["W2"])
+    for e in range(E):
+        lo, hi = int(r_off[e]), int(r_off[e + 1])
+        if lo == hi:
+            continue
+        ref = O.swiglu_expert(x[r_st[lo:hi]], W1s[e], W3s[e], W2s[e], faithful=True)
+        err = PY.rel_err(o_sum[lo:hi], ref)
+        say("expert %d: %d rows, rel err %.3e" % (e, hi - lo, err))
+        assert err <= PY.TOL_BF16, e
+
+
 def test_full_T512_sampled(dev):
     _full("mid_bf16_T512", dev, tokens=np.random.default_rng(1).choice(512, 32, replace=False))
 
