@@ -684,7 +684,7 @@ def main():
     ap.add_argument("--only", default=None, help="time just this workload (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only (the MoE layer is not sharded "
+        print("bench.py: this library runs on one GPU only (the MoE layer is not sharded "
               "across GPUs); --gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
     M.load_library()
