@@ -51,7 +51,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 typedef enum {
   MOE_OK = 0,
   MOE_EINVAL = 1,        /* bad pointer, size, K/E, aliasing, alignment */
-  MOE_EUNSUPPORTED = 2,  /* valid but not supported (e.g. bf16 d % 128 != 0) */
+  MOE_EUNSUPPORTED = 2,  /* valid but not supported (e.g. bf16 d % 64 != 0) */
   MOE_EWORKSPACE = 3,    /* workspace missing or smaller than moe_workspace_size */
   MOE_EHIP = 4           /* a HIP launch reported an error */
 } moe_status;
@@ -133,8 +133,11 @@ moe_status moe_workspace_layout(int64_t T, int64_t d, int64_t d_ff, int32_t E, i
  *   workspace   device buffer of at least moe_workspace_size bytes,
  *               256-byte aligned.
  * x must not overlap y.  T == 0 returns MOE_OK and launches nothing.
- * Limits: 1 <= K <= E <= 64; T*K < 2^31; bf16 needs d % 128 == 0,
- * d_ff % 128 == 0 and 16-byte aligned x, W*, y (else MOE_EUNSUPPORTED).
+ * Limits: 1 <= K <= E <= 64; T*K < 2^31; bf16 needs d % 64 == 0,
+ * d_ff % 64 == 0 and 16-byte aligned x, W*, y (else MOE_EUNSUPPORTED).
+ * Products whose sizes the streaming and tiled kernels cannot tile (they
+ * take multiples of 128 or 256) run the general grouped matrix-core
+ * kernels, which take multiples of 64.
  */
 moe_status moe_forward(const void* x, const void* W_g, const void* const* W1,
                        const void* const* W3, const void* const* W2, int64_t T, int64_t d,

@@ -296,7 +296,9 @@ hipError_t launch_expert_swiglu_bf16(const void* x, const int32_t* sorted_token,
   a.Kdim = d;
   a.N = d_ff;
   a.E = E;
-  if (d_ff % 128 == 0 && P > 0) return launch_cfg<256, 256, 64, true>(a, P, E, stream);
+  if (P <= 0) return hipSuccess;
+  if (d_ff % 128 == 0) return launch_cfg<256, 256, 64, true>(a, P, E, stream);
+  if (d_ff % 64 == 0) return launch_cfg<128, 256, 64, true>(a, P, E, stream);
   return hipErrorInvalidValue;
 }
 
@@ -313,7 +315,8 @@ hipError_t launch_expert_down_bf16(const void* H, const ExpertPtrs& W2, const in
   a.N = d;
   a.E = E;
   if (d % 256 == 0) return launch_cfg<256, 256, 64, false>(a, P, E, stream);
-  return launch_cfg<128, 256, 64, false>(a, P, E, stream);
+  if (d % 128 == 0) return launch_cfg<128, 256, 64, false>(a, P, E, stream);
+  return launch_cfg<64, 256, 64, false>(a, P, E, stream);
 }
 
 }  // namespace moe

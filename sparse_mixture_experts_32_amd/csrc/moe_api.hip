@@ -62,8 +62,8 @@ moe_status check_shape(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K,
   if (T * (int64_t)K >= (int64_t(1) << 31)) return fail(MOE_EINVAL, "T*K must be < 2^31");
   if (d >= (int64_t(1) << 31) || d_ff >= (int64_t(1) << 31))
     return fail(MOE_EINVAL, "d and d_ff must be < 2^31");
-  if (dt == MOE_BF16 && (d % 128 != 0 || d_ff % 128 != 0))
-    return fail(MOE_EUNSUPPORTED, "bf16 path needs d %% 128 == 0 and d_ff %% 128 == 0");
+  if (dt == MOE_BF16 && (d % 64 != 0 || d_ff % 64 != 0))
+    return fail(MOE_EUNSUPPORTED, "bf16 path needs d %% 64 == 0 and d_ff %% 64 == 0");
   return MOE_OK;
 }
 

@@ -91,6 +91,10 @@ def test_workspace_size_and_layout(lib):
     assert n.value >= lay["O"] + P * 4096 * 4
     assert lib.moe_workspace_size(8, 4096, 14336, 8, 2, 1, None) == EINVAL
     assert lib.moe_workspace_size(8, 4000, 14336, 8, 2, 1, ctypes.byref(n)) == EUNSUPPORTED
+    # bf16: multiples of 64 (the grouped kernels take what the others cannot tile)
+    assert lib.moe_workspace_size(8, 320, 448, 8, 2, 1, ctypes.byref(n)) == OK
+    assert lib.moe_workspace_size(8, 96, 448, 8, 2, 1, ctypes.byref(n)) == EUNSUPPORTED
+    assert lib.moe_workspace_size(8, 320, 480, 8, 2, 1, ctypes.byref(n)) == EUNSUPPORTED
     assert lib.moe_workspace_size(8, 4000, 14300, 8, 2, 0, ctypes.byref(n)) == OK  # fp32: any d
 
 

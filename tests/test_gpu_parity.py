@@ -280,6 +280,19 @@ def test_layer_bf16_small(dev, T, d, d_ff):
     check_layer(W.layer_inputs(w, dev), w.K)
 
 
+@pytest.mark.parametrize("T,d,d_ff", [(300, 320, 448), (24, 256, 320), (200, 192, 512),
+                                      (1, 64, 64)])
+def test_layer_bf16_multiples_of_64(dev, T, d, d_ff):
+    """bf16 shapes that are multiples of 64 but not of 128 (d or d_ff) take
+    the general grouped kernels: 128-column W1/W3 tiles when d_ff is an odd
+    multiple of 64, 64-column W2 tiles when d is."""
+    w = small(T=T, d=d, d_ff=d_ff)
+    plan = M.plan_for(T, d, d_ff, w.E, w.K, M.BF16)
+    say("layer bf16 multiples of 64", T, d, d_ff, plan)
+    assert not plan["streaming"] and plan["down_splits"] == 1
+    check_layer(W.layer_inputs(w, dev), w.K)
+
+
 @pytest.mark.parametrize("T,d,d_ff", [(8, 2048, 1024), (3, 1024, 2048), (32, 512, 1536),
                                       (8, 1024, 512), (1, 1024, 1024), (5, 1024, 2560),
                                       (16, 768, 2048)])
