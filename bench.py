@@ -549,13 +549,16 @@ def run_dense_reference(dev, steps=10, warmup=3):
     (torch.matmul).  T = 512: eight equal groups of 128 rows, one per
     expert, each against its own weights (torch.bmm over [8, ...] stacks:
     the same 1.88 GB and 0.94 GB of weights as the layer reads), reported
-    also as weight bytes per second."""
+    also as weight bytes per second.  And a square 8192^3 product: the
+    library's own rate on a shape it is best at, a practical ceiling for
+    bf16 matrix-core work on the part."""
     g = torch.Generator(device=dev).manual_seed(7)
     out = []
     for name, bsz, m, k, n in [("w1w3_dense", 1, 8192, 4096, 2 * 14336),
                                ("w2_dense", 1, 8192, 14336, 4096),
                                ("w1w3_8x128_batched", 8, 128, 4096, 2 * 14336),
-                               ("w2_8x128_batched", 8, 128, 14336, 4096)]:
+                               ("w2_8x128_batched", 8, 128, 14336, 4096),
+                               ("square_8192", 1, 8192, 8192, 8192)]:
         shape_a = (m, k) if bsz == 1 else (bsz, m, k)
         shape_b = (k, n) if bsz == 1 else (bsz, k, n)
         a = torch.randn(shape_a, generator=g, device=dev).to(torch.bfloat16)
