@@ -63,7 +63,7 @@ constexpr int kSlots = 4;      // LDS ring depth
 constexpr int kGroupF = 4;     // feature tiles interleaved in the tile order
 // W1/W3 chooses the tile shape per expert (tiled_mixed_kernel) up to this
 // average of rows per expert.  Against 256 x 256 tiles throughout, at Mixtral
-// shape with 8 experts (one box, 3 A/B pairs): 5.6, 7.3, 10.3, 11.2 and
+// shape with 8 experts (one machine, 3 A/B pairs): 5.6, 7.3, 10.3, 11.2 and
 // 5.7 % faster layers at 64, 128, 256, 384 and 512 tokens, level at 640 and
 // 768.  (The 128 x 512 tile for every expert was 3.4 % slower at 512 tokens:
 // three of the eight experts then hold more than 128 rows and would take a
