@@ -358,12 +358,12 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(StreamArgs a) {
 //
 // Work units are (busy token tile, feature tile of 256, matrix), numbered
 // u = (tile * tiles_f + ftile) * 2 + matrix, each K = Kdim rows long and cut
-// into chunks of kChunkRows rows (one k-step per wave).  With G workgroups
-// (one per compute unit):
+// into chunks of kChunkRows rows (one k-step per wave).  With G = kSkGrid
+// workgroups (one per compute unit on 7/8 of the compute units):
 //   * U >= G units: workgroup w takes chunks [w C / G, (w+1) C / G) of the
 //     C = U * (Kdim / kChunkRows) chunks in unit order, so every workgroup
 //     streams the same number of weight bytes (to one chunk: for
-//     Mixtral's shapes at 8 tokens, 49 chunks each) and no round of
+//     Mixtral's shapes at 8 tokens, 56 chunks each) and no round of
 //     workgroups is left nearly empty.  A unit is cut at most once; its head
 //     piece goes to partial-sum slice 0, its tail to slice 1.
 //   * U < G: every unit is cut into the same number s of pieces (the largest
@@ -375,6 +375,12 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(StreamArgs a) {
 // before the current piece's epilogue, and the epilogue synchronises the
 // waves through LDS only, so those loads stay in flight across it.
 constexpr int kChunkRows = 32 * kWaves;
+// Persistent workgroups of the stream-K launch.  Measured at Mixtral shape
+// with 8 tokens (one machine, 3 A/B rounds each): 224 workgroups stream the
+// W1/W3 weights 0.7-1 % faster than 256 (both divide Mixtral's chunk counts,
+// busy experts x 1792, evenly), 240 (uneven shares) 0.3 % slower than 256,
+// 168 and 112 8 % and 37 % slower.
+constexpr int kSkGrid = 224;
 
 __device__ __forceinline__ int sk_small_split(int U, int G, int cpu) {
   int s = 1;
@@ -663,14 +669,14 @@ int pick_launch(const double* wgs, int n) {
 }  // namespace
 
 // Partial-sum slices of the per-matrix W1/W3 product (stream_sk_kernel over
-// kComputeUnits workgroups): two for units cut by a workgroup boundary, or
+// kSkGrid workgroups): two for units cut by a workgroup boundary, or
 // the equal pieces of units when there are fewer units than workgroups (most
 // when a single token tile holds rows).
 int sk_slices(int d, int d_ff) {
   const int cpu = d / kChunkRows;
   const int U = 2 * (d_ff / kFeat);
   int s = 1;
-  while (cpu % (2 * s) == 0 && (int64_t)U * 2 * s <= (int64_t)kComputeUnits) s *= 2;
+  while (cpu % (2 * s) == 0 && (int64_t)U * 2 * s <= (int64_t)kSkGrid) s *= 2;
   return std::max(2, s);
 }
 
@@ -732,7 +738,7 @@ hipError_t launch_stream_swiglu_bf16(const void* x, const int32_t* sorted_token,
     return launch_stream<1, kFused>(a, stream);
   }
   if (P == 0) return hipSuccess;
-  hipLaunchKernelGGL(stream_sk_kernel, dim3((unsigned)kComputeUnits), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL(stream_sk_kernel, dim3((unsigned)kSkGrid), dim3(kThreads), 0, stream,
                      a);
   return hipGetLastError();
 }
@@ -743,7 +749,7 @@ hipError_t launch_swiglu_finish_bf16(const float* part, const int32_t* offsets, 
   if (n4 == 0) return hipSuccess;
   const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 2048);
   hipLaunchKernelGGL(swiglu_finish_kernel, dim3(blocks), dim3(256), 0, stream, part, offsets, E,
-                     P, d_ff, d, (int)kComputeUnits, static_cast<bf16_t*>(H));
+                     P, d_ff, d, kSkGrid, static_cast<bf16_t*>(H));
   return hipGetLastError();
 }
 
