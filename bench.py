@@ -221,7 +221,8 @@ def swiglu_kernel(plan):
         return "stream_sk_kernel", "expert_stream_bf16.hip"
     if plan.get("swiglu_mixed"):
         return "tiled_mixed_kernel", "expert_tiled_bf16.hip"
-    return "tiled_gemm_kernel<256, true, 256>", "expert_tiled_bf16.hip"
+    nt = "true" if plan.get("weights_nt") else "false"
+    return "tiled_gemm_kernel<256, true, 256, %s>" % nt, "expert_tiled_bf16.hip"
 
 
 def measured_traffic(workload, plan):

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 #define MOE_MAX_EXPERTS 64
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -77,6 +77,8 @@ typedef struct moe_plan {
   int32_t swiglu_mixed;         /* 1: the tiled W1/W3 product picks its tile shape per  */
                                 /* expert: 128 tokens x 512 columns for experts of at   */
                                 /* most 128 rows, 256 x 256 for the others              */
+  int32_t weights_nt;           /* 1: the tiled products read each weight tile once and */
+                                /* copy it with the non-temporal cache policy           */
 } moe_plan;
 
 /* Index of each intermediate inside the workspace; see moe_workspace_layout. */

@@ -66,13 +66,14 @@ _c_p = ctypes.c_void_p
 _c_sz = ctypes.c_size_t
 
 
-ABI_VERSION = 4   # MOE_ABI_VERSION of include/moe_mi355x.h that this binding speaks
+ABI_VERSION = 5   # MOE_ABI_VERSION of include/moe_mi355x.h that this binding speaks
 
 
 class _Plan(ctypes.Structure):
     _fields_ = [("swiglu_splits", ctypes.c_int32), ("down_splits", ctypes.c_int32),
                 ("swiglu_scratch_bytes", ctypes.c_size_t), ("streaming", ctypes.c_int32),
-                ("down_scratch_bytes", ctypes.c_size_t), ("swiglu_mixed", ctypes.c_int32)]
+                ("down_scratch_bytes", ctypes.c_size_t), ("swiglu_mixed", ctypes.c_int32),
+                ("weights_nt", ctypes.c_int32)]
 
 
 def load_library(path: str | None = None):
@@ -180,7 +181,8 @@ def plan_for(T, d, d_ff, E, K, dtype) -> dict:
     _check(lib.moe_plan_for(T, d, d_ff, E, K, dtype, ctypes.byref(p)), lib)
     return dict(swiglu_splits=p.swiglu_splits, down_splits=p.down_splits,
                 swiglu_scratch_bytes=p.swiglu_scratch_bytes, streaming=bool(p.streaming),
-                down_scratch_bytes=p.down_scratch_bytes, swiglu_mixed=bool(p.swiglu_mixed))
+                down_scratch_bytes=p.down_scratch_bytes, swiglu_mixed=bool(p.swiglu_mixed),
+                weights_nt=bool(p.weights_nt))
 
 
 def workspace_size(T, d, d_ff, E, K, dtype) -> int:

@@ -199,6 +199,7 @@ moe_status moe_plan_for(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t K
   plan->swiglu_scratch_bytes = p.scratch;
   plan->down_scratch_bytes = p.down_scratch;
   plan->swiglu_mixed = p.swiglu_mixed ? 1 : 0;
+  plan->weights_nt = dtype == MOE_BF16 && !p.streaming && T > 0 && moe::weights_read_once(T * K, E);
   plan->streaming = p.streaming ? 1 : 0;
   return ok();
 }

@@ -90,6 +90,10 @@ int tiled_gemm_tiles(int P, int E, int N, bool dual);  // worst-case workgroups 
 // Whether the tiled W1/W3 launch chooses its tile shape per expert (128 x 512
 // for experts of at most 128 rows, 256 x 256 otherwise).
 bool tiled_swiglu_mixed(int P, int E, int d_ff);
+// Whether the tiled products copy weights with the non-temporal cache policy
+// (each expert's rows fill about one token tile, so each weight tile is read
+// once).
+bool weights_read_once(int64_t P, int E);
 hipError_t launch_tiled_swiglu_bf16(const void* x, const int32_t* sorted_token,
                                     const ExpertPtrs& W1, const ExpertPtrs& W3,
                                     const int32_t* offsets, int P, int d, int d_ff, int E,

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 4 == M.ABI_VERSION
+    assert lib.moe_abi_version() == 5 == M.ABI_VERSION
     assert lib.moe_status_str(0) == b"MOE_OK"
     assert lib.moe_status_str(4) == b"MOE_EHIP"
 
@@ -72,6 +72,12 @@ def test_plan(lib):
     assert p["down_splits"] > 1 and p["down_scratch_bytes"] == 0 and p["swiglu_mixed"]
     assert not M.plan_for(1024, 4096, 14336, 8, 2, M.BF16)["swiglu_mixed"]
     assert not M.plan_for(512, 4096, 14208, 8, 2, M.BF16)["swiglu_mixed"]   # d_ff % 256
+    # weight tiles read once (non-temporal copies) up to 192 rows per expert
+    assert M.plan_for(512, 4096, 14336, 8, 2, M.BF16)["weights_nt"]
+    assert M.plan_for(768, 4096, 14336, 8, 2, M.BF16)["weights_nt"]
+    assert not M.plan_for(769, 4096, 14336, 8, 2, M.BF16)["weights_nt"]
+    assert not M.plan_for(4096, 4096, 14336, 8, 2, M.BF16)["weights_nt"]
+    assert not M.plan_for(8, 4096, 14336, 8, 2, M.BF16)["weights_nt"]     # streaming
     # the tiled W2 kernel addresses its token operand (H) with 32-bit byte
     # offsets: at d_ff = 65536, 32000 rows fit (K split 4), 33000 do not and
     # W2 falls back to the unsplit grouped kernel

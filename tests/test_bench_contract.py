@@ -51,7 +51,7 @@ def test_roofline_object_is_flops_over_time_against_the_mfma_peak():
     r = bench.roofline_for(w, a, {"expert_swiglu": 1.7}, plan)
     assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
     assert r["achieved"] == pytest.approx(a["swiglu_flops"] / 1.7e-3 / 1e12, rel=1e-3)
-    assert r["kernel"] == "tiled_gemm_kernel<256, true, 256>"
+    assert r["kernel"] == "tiled_gemm_kernel<256, true, 256, false>"
 
 
 def test_w1w3_kernel_name_follows_the_plan():
@@ -60,7 +60,7 @@ def test_w1w3_kernel_name_follows_the_plan():
     assert bench.swiglu_kernel(dict(streaming=False, swiglu_splits=0))[1] == "expert_tiled_bf16.hip"
     assert bench.swiglu_kernel(M.plan_for(512, 4096, 14336, 8, 2, M.BF16))[0] == "tiled_mixed_kernel"
     assert (bench.swiglu_kernel(M.plan_for(4096, 4096, 14336, 8, 2, M.BF16))[0]
-            == "tiled_gemm_kernel<256, true, 256>")
+            == "tiled_gemm_kernel<256, true, 256, false>")
 
 
 def test_committed_counters_are_found_only_for_their_kernel_and_workload():
