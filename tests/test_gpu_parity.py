@@ -518,15 +518,15 @@ def test_w2_split_tail_every_row(dev):
 def test_tile_shape_per_expert_boundaries(dev, counts):
     """The W1/W3 product with a tile shape per expert (128 x 512 tiles for
     experts of at most 128 rows, 256 x 256 otherwise) and the K-split W2
-    product, on routing built by hand: experts of 0, 1, 128, 129, 256 and 257
-    rows; only 256-row tiles; only the wide shape.  Token i takes the experts
-    of entries i and i + T of the sorted label list (distinct, since no
-    expert holds T or more pairs).  Each expert's output rows (the W2 slices
-    summed) are compared with the oracle's expert on the same token rows."""
+    product, on routing built by hand: experts of 0, 1, 128, 129, 256 and 257 rows; only
+    256-row tiles; only the wide shape.  Token i takes the experts of entries
+    i and i + T of the sorted label list (distinct, since no expert holds T
+    or more pairs).  Each expert's output rows (the W2 slices summed) are
+    compared with the oracle's expert on the same token rows."""
     E, K = len(counts), 2
     P = sum(counts)
     T = P // K
-    w = small(T=T, d=256, d_ff=512, E=E)
+    w = small(T=T, d=512, d_ff=512, E=E)
     plan = M.plan_for(T, w.d, w.d_ff, E, K, M.BF16)
     say("tile shape per expert", counts, plan)
     assert plan["swiglu_mixed"] and not plan["streaming"]
