@@ -567,32 +567,57 @@ hipError_t launch_tiled(const TiledArgs& in, int P, hipStream_t stream) {
 }
 
 // O rows of the tail tiles of a split W2 launch: the sum of the tile's S
-// pieces in piece order.  One block per (tail tile, 4 rows), a thread per 4
-// features.
+// pieces in piece order.  A fixed grid of kFixupBlocks blocks, each reading
+// the expert offsets into LDS and working out the tail plan once; items are
+// (tail tile, 4 rows), a thread per 4 features, and a block takes items
+// blockIdx.x + j gridDim.x four at a time, so that the loads of four items
+// are in flight together.
+constexpr int kFixupBlocks = 768;
+constexpr int kFixupBatch = 4;
+
 __global__ __launch_bounds__(256) void tail_fixup_kernel(const float* __restrict__ side,
                                                          int side_rows, int side_pieces,
                                                          const int32_t* __restrict__ offsets,
                                                          int E, int N, int Kdim, int group_f,
                                                          float* __restrict__ O) {
-  constexpr int kRowsPerBlock = 256 / (kBF / 4);
+  constexpr int kRowsPerItem = 256 / (kBF / 4);
+  __shared__ int32_t off[kMaxExperts + 1];
+  if ((int)threadIdx.x <= E) off[threadIdx.x] = offsets[threadIdx.x];
+  __syncthreads();
   const int tiles_f = N / kBF;
   int bt, nt, Nw, S;
-  tail_plan(offsets, E, tiles_f, Kdim, side_pieces, bt, nt, Nw, S);
-  const int blocks_per_tile = (side_rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  const int t = blockIdx.x / blocks_per_tile;   // tail tile
-  if (S == 1 || t >= nt - Nw) return;
-  const int i = (blockIdx.x % blocks_per_tile) * kRowsPerBlock + threadIdx.x / (kBF / 4);
+  tail_plan(off, E, tiles_f, Kdim, side_pieces, bt, nt, Nw, S);
+  if (S == 1) return;
+  const int groups = (side_rows + kRowsPerItem - 1) / kRowsPerItem;
+  const int items = (nt - Nw) * groups;
+  const int sub = threadIdx.x / (kBF / 4);
   const int c = (threadIdx.x % (kBF / 4)) * 4;
-  int ftile, ttile, e, rb, re;
-  tail_tile(Nw + t, bt, group_f, ftile, ttile);
-  if (!find_tile(offsets, E, 256, ttile, e, rb, re) || i >= min(256, re - rb)) return;
-  const float* src = side + ((int64_t)t * S * side_rows + i) * kBF + c;
-  float4 a = *reinterpret_cast<const float4*>(src);
-  for (int q = 1; q < S; ++q) {
-    const float4 x = *reinterpret_cast<const float4*>(src + (int64_t)q * side_rows * kBF);
-    a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+  const int64_t piece_stride = (int64_t)side_rows * kBF;
+  for (int i0 = blockIdx.x; i0 < items; i0 += kFixupBatch * gridDim.x) {
+    float4 a[kFixupBatch];
+    int64_t dst[kFixupBatch];
+#pragma unroll
+    for (int q = 0; q < kFixupBatch; ++q) {
+      dst[q] = -1;
+      const int item = i0 + q * gridDim.x;
+      if (item >= items) continue;
+      const int t = item / groups;   // tail tile
+      const int i = (item % groups) * kRowsPerItem + sub;
+      int ftile, ttile, e, rb, re;
+      tail_tile(Nw + t, bt, group_f, ftile, ttile);
+      if (!find_tile(off, E, 256, ttile, e, rb, re) || i >= min(256, re - rb)) continue;
+      const float* src = side + ((int64_t)t * S * side_rows + i) * kBF + c;
+      a[q] = *reinterpret_cast<const float4*>(src);
+      for (int p = 1; p < S; ++p) {
+        const float4 x = *reinterpret_cast<const float4*>(src + p * piece_stride);
+        a[q].x += x.x; a[q].y += x.y; a[q].z += x.z; a[q].w += x.w;
+      }
+      dst[q] = (int64_t)(rb + i) * N + ftile * kBF + c;
+    }
+#pragma unroll
+    for (int q = 0; q < kFixupBatch; ++q)
+      if (dst[q] >= 0) *reinterpret_cast<float4*>(O + dst[q]) = a[q];
   }
-  *reinterpret_cast<float4*>(O + (int64_t)(rb + i) * N + ftile * kBF + c) = a;
 }
 
 }  // namespace
@@ -701,10 +726,8 @@ hipError_t launch_tiled_down_fixup(const float* side, size_t side_bytes, const i
   const int rows = std::min(256, P);
   const int pieces = (int)std::min<size_t>(kTailRound, side_bytes / ((size_t)rows * kBF * 4));
   if (pieces < 2) return hipSuccess;
-  // at most kTailRound / 2 tail tiles (two pieces or more each)
-  const int blocks = kTailRound / 2 * ((rows + 3) / 4);
-  hipLaunchKernelGGL(tail_fixup_kernel, dim3(blocks), dim3(256), 0, stream, side, rows, pieces,
-                     offsets, E, d, d_ff, group_for(d / kBF), O);
+  hipLaunchKernelGGL(tail_fixup_kernel, dim3(kFixupBlocks), dim3(256), 0, stream, side, rows,
+                     pieces, offsets, E, d, d_ff, group_for(d / kBF), O);
   return hipGetLastError();
 }
 
