@@ -31,6 +31,7 @@ import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+NOMINAL_SCLK_GHZ = 2.4          # the clock behind the 2.5 PFLOP/s figure
 HEADLINE = "decode_bf16_T8"
 SWEEP = ("mid_bf16_T512", "prefill_bf16_T4096_zipf")
 DECODE_SWEEP_T = (1, 2, 4, 16, 32, 64)
@@ -264,6 +265,28 @@ def traced_avg_ms(workload, plan):
     return None
 
 
+TILED_COUNTERS = os.path.join(ROOT, "profiles", "prefill_bf16_T4096_zipf_tiled_counters.txt")
+
+
+def measured_sclk(kernel, src):
+    """Clock (GHz) the kernel ran at in the committed core-counter summary
+    (GRBM_GUI_ACTIVE per XCD over the traced duration), or None when it has no
+    row for the kernel or the kernel's source changed since."""
+    try:
+        import hashlib
+        sha = hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest()
+        text = open(TILED_COUNTERS).read()
+    except OSError:
+        return None
+    if ("%s: %s" % (src, sha)) not in text:
+        return None
+    for ln in text.splitlines():
+        r = [c.strip() for c in ln.split("|")]
+        if not ln.startswith("#") and len(r) >= 3 and r[0] == kernel:
+            return float(r[2])
+    return None
+
+
 def roofline_for(w, alg, per_stage_ms, plan):
     """Roofline object of the W1/W3 kernel: `frac` from its HIP-event time in
     this run, `frac_trace` from the average duration in the committed kernel
@@ -284,6 +307,12 @@ def roofline_for(w, alg, per_stage_ms, plan):
                trace_avg_ms=None if tr_ms is None else round(tr_ms, 4),
                frac_trace=None if tr_ms is None else round(work / (tr_ms * 1e-3) / scale / peak,
                                                            4))
+    if bound == "mfma":
+        # the matrix peak at the clock the part held under this kernel
+        sclk = measured_sclk(kernel, swiglu_kernel(plan)[1])
+        if sclk is not None:
+            at = peak * sclk / NOMINAL_SCLK_GHZ
+            out.update(sclk_ghz=sclk, peak_at_sclk=round(at, 1), frac_at_sclk=round(achieved / at, 4))
     return out
 
 

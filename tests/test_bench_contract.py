@@ -52,6 +52,10 @@ def test_roofline_object_is_flops_over_time_against_the_mfma_peak():
     assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
     assert r["achieved"] == pytest.approx(a["swiglu_flops"] / 1.7e-3 / 1e12, rel=1e-3)
     assert r["kernel"] == "tiled_gemm_kernel<256, true, 256, false>"
+    if "sclk_ghz" in r:          # while the committed counters match the kernel source
+        assert 1.0 < r["sclk_ghz"] < 2.5
+        assert r["peak_at_sclk"] == pytest.approx(2500.0 * r["sclk_ghz"] / 2.4, rel=1e-3)
+        assert r["frac_at_sclk"] == pytest.approx(r["achieved"] / r["peak_at_sclk"], rel=1e-3)
 
 
 def test_w1w3_kernel_name_follows_the_plan():
