@@ -442,6 +442,27 @@ ATTN_COUNTERS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profil
                              "attn_counters.txt")
 
 
+def attn_sclk(kernel, workload):
+    """Clock (GHz) the attention kernel ran at in the committed counters, or
+    None (no clock for short dispatches, or swa_attention.hip changed)."""
+    try:
+        import hashlib
+        sha = hashlib.sha256(open(os.path.join(CSRC, "swa_attention.hip"), "rb").read()).hexdigest()
+        text = open(ATTN_COUNTERS).read()
+    except OSError:
+        return None
+    if ("swa_attention.hip: " + sha) not in text:
+        return None
+    for ln in text.splitlines():
+        r = [c.strip() for c in ln.split("|")]
+        if not ln.startswith("#") and len(r) >= 7 and r[0] == kernel and r[1] == workload:
+            try:
+                return float(r[6])
+            except ValueError:
+                return None
+    return None
+
+
 def attn_traffic(kernel, workload):
     """Calibrated FETCH+WRITE bytes per dispatch of the attention kernel, or
     None when no row matches or swa_attention.hip changed since the counters
@@ -523,6 +544,11 @@ def run_attention(dev, steps, warmup, cpu=True):
                                  peak=peak, unit="GB/s" if bound == "hbm" else "TFLOP/s",
                                  frac=round(achieved / peak, 4),
                                  traffic=attn_traffic(kernel, name)))
+        sclk = attn_sclk(kernel, name) if bound == "mfma" else None
+        if sclk is not None:
+            at = peak * sclk / NOMINAL_SCLK_GHZ
+            res["roofline"].update(sclk_ghz=sclk, peak_at_sclk=round(at, 1),
+                                   frac_at_sclk=round(achieved / at, 4))
         if cpu and w.T == 1:
             from oracle import swa_oracle as A
             t0 = time.perf_counter()

@@ -80,3 +80,14 @@ def test_committed_counters_are_found_only_for_their_kernel_and_workload():
         # of W1/W3 weights, plus the token rows and partial sums
         assert 1.60e9 < got < 1.75e9
     assert bench.measured_traffic("no_such_workload", plan) is None
+
+
+def test_attention_clock_comes_from_the_committed_counters_of_its_source():
+    """The prefill attention row of the committed counters carries the clock
+    the part held under the kernel; decode's dispatches are too short for one.
+    None for any other kernel or workload."""
+    got = bench.attn_sclk("swa_attn_kernel<2>", "attn_prefill_bf16_T4096")
+    if got is not None:          # None only while swa_attention.hip changed since profiling
+        assert 1.0 < got < 2.5
+    assert bench.attn_sclk("swa_attn_kernel<1>", "attn_decode_bf16_B8") is None
+    assert bench.attn_sclk("swa_attn_kernel<2>", "no_such_workload") is None
