@@ -78,7 +78,8 @@ typedef struct moe_plan {
                                 /* expert: 128 tokens x 512 columns for experts of at   */
                                 /* most 128 rows, 256 x 256 for the others              */
   int32_t weights_nt;           /* 1: the tiled products read each weight tile once and */
-                                /* copy it with the non-temporal cache policy           */
+                                /* copy it with the non-temporal cache policy (0: only  */
+                                /* the copies of experts that fit one token tile are)   */
 } moe_plan;
 
 /* Index of each intermediate inside the workspace; see moe_workspace_layout. */

@@ -41,7 +41,8 @@
 //     are interleaved with the token tiles, so the ~32 workgroups it runs at
 //     once share a few weight tiles and a few token tiles in its L2;
 //   * where every expert holds about one token tile of rows, each weight
-//     tile is read once and its copies are non-temporal (weights_read_once).
+//     tile is read once and its copies are non-temporal (weights_read_once);
+//     elsewhere so are those of any expert whose rows fit one token tile.
 #include <algorithm>
 #include <type_traits>
 
@@ -482,7 +483,12 @@ __global__ __launch_bounds__(512) void tiled_gemm_kernel(TiledArgs args) {
   int e, row_begin, row_end;
   if (!find_tile(args.offsets, args.E, BT, ttile, e, row_begin, row_end)) return;
 
-  tile_body<BT, DUAL, BF, NT>(args, sW, sA, e, row_begin, row_end, ftile, split, nsplit, piece);
+  // An expert whose rows fit one token tile has each weight tile read once:
+  // its copies are non-temporal even where the launch's are not.
+  if (NT || args.offsets[e + 1] - args.offsets[e] <= BT)
+    tile_body<BT, DUAL, BF, true>(args, sW, sA, e, row_begin, row_end, ftile, split, nsplit, piece);
+  else
+    tile_body<BT, DUAL, BF, false>(args, sW, sA, e, row_begin, row_end, ftile, split, nsplit, piece);
 }
 
 // W1/W3 with a tile shape per expert: experts of at most 128 rows take one
@@ -493,8 +499,9 @@ __global__ __launch_bounds__(512) void tiled_gemm_kernel(TiledArgs args) {
 // share of the wide units first (the longer ones), then its share of the
 // 256-row units, so the XCDs stay balanced and each reuses a few weight and
 // token tiles from its L2.  The four 40 KB LDS slots hold either shape.  It
-// runs only where weights_read_once holds, so its weight copies are
-// non-temporal.
+// runs only where weights_read_once holds; weight copies are non-temporal
+// except for an expert of more than one 256-row tile (skewed routing), whose
+// tiles share its weight tiles.
 constexpr int kMixedSlot = 40 * 1024;
 
 __global__ __launch_bounds__(512) void tiled_mixed_kernel(TiledArgs args) {
@@ -546,7 +553,10 @@ __global__ __launch_bounds__(512) void tiled_mixed_kernel(TiledArgs args) {
   } else {
     char* const sW[kSlots] = {s0, s1, s2, s3};
     char* const sA[kSlots] = {s0 + CS::kSlotW, s1 + CS::kSlotW, s2 + CS::kSlotW, s3 + CS::kSlotW};
-    tile_body<256, true, 256, true>(args, sW, sA, e, row_begin, row_end, ftile, 0, 1, -1);
+    if (row_end - args.offsets[e] <= 256)   // one token tile: weights read once
+      tile_body<256, true, 256, true>(args, sW, sA, e, row_begin, row_end, ftile, 0, 1, -1);
+    else
+      tile_body<256, true, 256, false>(args, sW, sA, e, row_begin, row_end, ftile, 0, 1, -1);
   }
 }
 
