@@ -570,9 +570,12 @@ moe_status moe_stack_forward(void* h, const void* const* W_g, const void* const*
   const Plan plan = make_plan(T, d, d_ff, E, K, dtype);
   const int64_t slice = T * K * d;
   // Small batches join the blocks with one glue launch (the previous block's
-  // combine, RMSNorm, this block's router); otherwise RMSNorm, router and
-  // combine are launched one by one.  Both run the same arithmetic.
+  // combine, RMSNorm, this block's router).  Otherwise the previous block's
+  // combine and the RMSNorm share one launch where they can (bf16), and the
+  // router follows; else all three are launched one by one.  All run the
+  // same arithmetic.
   const bool glue = plan.streaming && moe::stack_glue_supported((int)T, (int)d, E, dtype);
+  const bool norm = !glue && moe::stack_norm_supported((int)d, dtype);
   hipError_t e = hipSuccess;
   for (int l = 0; l < L; ++l) {
     moe::ExpertPtrs p1, p3, p2;
@@ -584,7 +587,9 @@ moe_status moe_stack_forward(void* h, const void* const* W_g, const void* const*
                                  b.pos, b.topk_idx, W_g[l], (int)T, (int)d, E, K, eps, st);
       if (e != hipSuccess) return hip_status(e, "stack_glue");
     } else {
-      e = moe::launch_rmsnorm(h, xn, (int)T, (int)d, eps, dtype, st);
+      e = norm ? moe::launch_stack_norm(h, xn, l > 0 ? b.O : nullptr, plan.down_splits, slice,
+                                        b.topk_w, b.pos, (int)T, (int)d, K, eps, st)
+               : moe::launch_rmsnorm(h, xn, (int)T, (int)d, eps, dtype, st);
       if (e != hipSuccess) return hip_status(e, "rmsnorm");
       e = moe::launch_router_topk(xn, W_g[l], (int)T, (int)d, E, K, dtype, b.topk_idx, b.topk_w,
                                   nullptr, st);
@@ -596,7 +601,7 @@ moe_status moe_stack_forward(void* h, const void* const* W_g, const void* const*
       if (e != hipSuccess) return hip_status(e, "routing_stats");
     }
     if ((s = run_experts(plan, xn, p1, p3, p2, b, T, d, d_ff, E, K, dtype, st))) return s;
-    if (!glue || l == L - 1) {
+    if (!(glue || norm) || l == L - 1) {
       e = moe::launch_combine(b.O, plan.down_splits, slice, b.topk_w, b.pos, (int)T, (int)d, K, h,
                               dtype, 1, st);
       if (e != hipSuccess) return hip_status(e, "combine");

@@ -26,6 +26,14 @@ bool stack_glue_supported(int T, int d, int E, int dtype);
 hipError_t launch_stack_glue(void* h, void* xn, const float* O, int o_splits, int64_t slice,
                              float* topk_w, const int32_t* pos, int32_t* topk_idx, const void* Wg,
                              int T, int d, int E, int K, float eps, hipStream_t stream);
+// The glue without the router, for any batch: [the previous block's combine
+// into h with the residual add, when O is not null] and RMSNorm of h into xn,
+// one workgroup per token.  Bit-identical to launch_combine(accumulate) +
+// launch_rmsnorm.  Needs stack_norm_supported().
+bool stack_norm_supported(int d, int dtype);
+hipError_t launch_stack_norm(void* h, void* xn, const float* O, int o_splits, int64_t slice,
+                             const float* topk_w, const int32_t* pos, int T, int d, int K,
+                             float eps, hipStream_t stream);
 
 hipError_t launch_route_permute(const int32_t* topk_idx, int T, int E, int K, int32_t* offsets,
                                 int32_t* sorted_token, int32_t* pos, hipStream_t stream);

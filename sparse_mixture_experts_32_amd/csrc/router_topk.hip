@@ -298,11 +298,13 @@ __global__ __launch_bounds__(256) void router_e8_kernel(const bf16_t* __restrict
 //      order (read back from LDS), then a fixed tree over those 256 sums,
 //      xn = round(h / sqrt(mean + eps)) -- the arithmetic of the RMSNorm
 //      kernel;
-//   3. the next block's router on xn, held in LDS, by the first four
+//   3. (ROUTE) the next block's router on xn, held in LDS, by the first four
 //      wavefronts -- the arithmetic of the router kernel with four
 //      wavefronts per token.  Their first W_g rows are loaded at the start of
-//      the kernel, so those loads overlap steps 1 and 2.
-// The results are those of the three separate kernels, bit for bit.  Token
+//      the kernel, so those loads overlap steps 1 and 2.  Without ROUTE
+//      (large batches, whose router is the many-token kernel, launched
+//      after this one) the kernel ends after step 2.
+// The results are those of the separate kernels, bit for bit.  Token
 // t's previous gate weights and positions are read in step 1, before the
 // barriers after which wave 0 overwrites them with the new ones, and by the
 // workgroup of token t only.
@@ -311,7 +313,7 @@ constexpr int kGluePrefetch = 2;     // 8-row W_g chunks held per router thread
 constexpr int kGlueRanks = 2;        // the combine's loads are all issued at once for
 constexpr int kGlueSlices = 4;       // K <= kGlueRanks and splits <= kGlueSlices
 
-template <bool COMBINE>
+template <bool COMBINE, bool ROUTE>
 __global__ __launch_bounds__(kGlueThreads) void stack_glue_kernel(
     bf16_t* __restrict__ h, bf16_t* __restrict__ xn, const float* __restrict__ O, int splits,
     int64_t slice, float* __restrict__ topk_w, const int32_t* __restrict__ pos,
@@ -333,7 +335,7 @@ __global__ __launch_bounds__(kGlueThreads) void stack_glue_kernel(
     const int k0 = tid * 8 + q * 256 * 8;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      wpre[q][i] = (router && k0 < d) ? *reinterpret_cast<const uint4*>(Wg + (int64_t)(k0 + i) * E)
+      wpre[q][i] = (ROUTE && router && k0 < d) ? *reinterpret_cast<const uint4*>(Wg + (int64_t)(k0 + i) * E)
                                       : make_uint4(0, 0, 0, 0);
   }
 
@@ -456,6 +458,7 @@ __global__ __launch_bounds__(kGlueThreads) void stack_glue_kernel(
     *reinterpret_cast<uint2*>(xs + c) = xb;
     *reinterpret_cast<uint2*>(xr + c) = xb;
   }
+  if constexpr (!ROUTE) return;   // the next block's router runs as its own launch
   __syncthreads();
 
   // the router kernel's vector path with TPT = 256 (see vec_partials): the
@@ -516,17 +519,45 @@ hipError_t launch_stack_glue(void* h, void* xn, const float* O, int o_splits, in
                              int T, int d, int E, int K, float eps, hipStream_t stream) {
   const int lds = d * (int)sizeof(bf16_t);
   if (O) {
-    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(&stack_glue_kernel<true>), lds);
+    hipError_t e =
+        allow_dynamic_lds(reinterpret_cast<const void*>(&stack_glue_kernel<true, true>), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(stack_glue_kernel<true>, dim3(T), dim3(kGlueThreads), lds, stream,
+    hipLaunchKernelGGL((stack_glue_kernel<true, true>), dim3(T), dim3(kGlueThreads), lds, stream,
                        static_cast<bf16_t*>(h), static_cast<bf16_t*>(xn), O, o_splits, slice,
                        topk_w, pos, topk_idx, static_cast<const bf16_t*>(Wg), d, E, K, eps);
   } else {
-    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(&stack_glue_kernel<false>), lds);
+    hipError_t e =
+        allow_dynamic_lds(reinterpret_cast<const void*>(&stack_glue_kernel<false, true>), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(stack_glue_kernel<false>, dim3(T), dim3(kGlueThreads), lds, stream,
+    hipLaunchKernelGGL((stack_glue_kernel<false, true>), dim3(T), dim3(kGlueThreads), lds, stream,
                        static_cast<bf16_t*>(h), static_cast<bf16_t*>(xn), nullptr, 1, 0, topk_w,
                        nullptr, topk_idx, static_cast<const bf16_t*>(Wg), d, E, K, eps);
+  }
+  return hipGetLastError();
+}
+
+bool stack_norm_supported(int d, int dtype) {
+  return dtype == kBF16 && d % 8 == 0 && d <= kStackGlueMaxD;
+}
+
+hipError_t launch_stack_norm(void* h, void* xn, const float* O, int o_splits, int64_t slice,
+                             const float* topk_w, const int32_t* pos, int T, int d, int K,
+                             float eps, hipStream_t stream) {
+  const int lds = d * (int)sizeof(bf16_t);
+  if (O) {
+    hipError_t e =
+        allow_dynamic_lds(reinterpret_cast<const void*>(&stack_glue_kernel<true, false>), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((stack_glue_kernel<true, false>), dim3(T), dim3(kGlueThreads), lds, stream,
+                       static_cast<bf16_t*>(h), static_cast<bf16_t*>(xn), O, o_splits, slice,
+                       const_cast<float*>(topk_w), pos, nullptr, nullptr, d, 0, K, eps);
+  } else {
+    hipError_t e =
+        allow_dynamic_lds(reinterpret_cast<const void*>(&stack_glue_kernel<false, false>), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((stack_glue_kernel<false, false>), dim3(T), dim3(kGlueThreads), lds,
+                       stream, static_cast<bf16_t*>(h), static_cast<bf16_t*>(xn), nullptr, 1, 0,
+                       nullptr, nullptr, nullptr, nullptr, d, 0, K, eps);
   }
   return hipGetLastError();
 }

@@ -691,14 +691,17 @@ def test_stack_graph_replay_matches_eager(dev, T):
 
 @pytest.mark.parametrize("E,K,T,d,d_ff", [(6, 2, 8, 512, 256), (16, 4, 8, 512, 256),
                                           (8, 2, 1, 512, 256), (8, 2, 2, 4096, 14336),
-                                          (8, 2, 4, 4096, 14336), (8, 2, 8, 4096, 14336)])
+                                          (8, 2, 4, 4096, 14336), (8, 2, 8, 4096, 14336),
+                                          (8, 2, 1100, 512, 256), (8, 3, 700, 384, 256)])
 def test_stack_glue_and_separate_launches_agree(dev, E, K, T, d, d_ff):
-    """The stack joins blocks with one glue launch when it can (8 | E) and
-    launches RMSNorm, router and combine separately otherwise; either way the
+    """The stack joins small-batch blocks with one glue launch when it can
+    (8 | E); otherwise the previous block's combine and the RMSNorm share one
+    launch and the router follows (E = 6, and the tiled batches of 700 and
+    1100 tokens, the latter with the many-token router).  Either way the
     stack equals moe_rmsnorm + moe_forward(accumulate) block by block, bit
     for bit.  The Mixtral-shape cases give the W2 product 4 and 2 slices (the
-    glue's all-loads-first combine); K = 4 and 7 slices (T = 1) take its
-    general loop."""
+    glue's all-loads-first combine); K = 4, K = 3 and 7 slices (T = 1) take
+    its general loop."""
     w = small(name="stack32_bf16_T4096", T=T, d=d, d_ff=d_ff, E=E, K=K)
     say("stack glue", E, K, T, d, d_ff, M.plan_for(T, d, d_ff, E, K, M.BF16))
     h0, blocks = _stack_inputs(w, dev, 3)
